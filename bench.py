@@ -1,0 +1,340 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+Headline workload (the metric's first half): the Qwen3-0.6B-shaped decode
+step -- 64 sequences, H_q=16, H_kv=8, D=128, bf16, block size 256, a shuffled
+pool of 4096 blocks, context lengths uniform in [128, 4096]. One step is
+pa_store_kvcache of the 64 new tokens followed by pa_decode over every
+sequence's whole history. Inputs are generated on the device (seed 0) before
+timing; an untimed 1 GiB write evicts L2/MALL before each step so every step
+reads its KV cold, as a layer's KV would be in a real model step.
+
+Also measured in the same run (unless --quick): the chunked varlen prefill
+workload (16384 query tokens over 24 sequences with shared cached prefixes:
+store + pa_prefill_varlen; the metric's second half), the 8B-shaped
+large-batch decode at block sizes 16 and 256, and the 131072-token
+long-context split-K decode.
+
+Prints one JSON line. `value` = decode algorithmic bytes per step / step
+time. `roofline` describes the decode call (the dominant kernel) timed with
+HIP events on the stream it runs on. `cpu_baseline` times the fp64 oracle on
+the host over a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
+METRIC = "decode KV-read GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak), 1 GPU"
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_66_amd", "csrc", "decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget")
+    ap.add_argument("--partition", type=int, default=0, help="decode partition (0 = library default)")
+    return ap.parse_args()
+
+
+def kernel_sha(path=DECODE_SRC):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def stored_traffic():
+    """Per-launch HBM bytes of the decode call from committed rocprofv3 --pmc
+    runs, or None when absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha256") != kernel_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Timer:
+    """Per-step HIP events on the current stream."""
+
+    def __init__(self, torch, n, marks):
+        self.torch = torch
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(marks)] for _ in range(n)]
+
+    def rec(self, step, mark):
+        self.ev[step][mark].record()
+
+    def span(self, a, b):
+        return [e[a].elapsed_time(e[b]) for e in self.ev]
+
+
+def run_decode(torch, binding, wl, w, steps, warmup, flush, scratch, partition=0, label=None):
+    t = wl.make_device_tensors(w)
+    slots = torch.from_numpy(w.slot_mapping).cuda()
+    tables = torch.from_numpy(w.block_tables).cuda()
+    ctx = torch.from_numpy(w.context_lens).cuda()
+    out = torch.empty_like(t["q"].contiguous())
+    need = binding.pa_decode_workspace_size(w.num_seqs, w.num_q_heads, w.head_dim, w.block_size,
+                                            w.max_blocks_per_seq, partition)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        binding.pa_store_kvcache(t["k"], t["v"], t["k_cache"], t["v_cache"], slots)
+
+    def dec():
+        binding.pa_decode(t["q"], t["k_cache"], t["v_cache"], tables, ctx, w.scale, out=out,
+                          workspace=ws, partition_size=partition)
+
+    for _ in range(warmup):
+        step()
+        dec()
+    torch.cuda.synchronize()
+    timer = Timer(torch, steps, 3)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        if flush:
+            scratch.zero_()
+        timer.rec(s, 0)
+        step()
+        timer.rec(s, 1)
+        dec()
+        timer.rec(s, 2)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = timer.span(0, 2)
+    dec_ms = timer.span(1, 2)
+    store_ms = timer.span(0, 1)
+    assert bool(torch.isfinite(out.float()).all()), f"{w.name}: non-finite decode output"
+    res = dict(
+        workload=label or w.name,
+        step_ms=sum(step_ms) / steps,
+        decode_ms=sum(dec_ms) / steps,
+        decode_ms_p10_p90=[sorted(dec_ms)[steps // 10], sorted(dec_ms)[(9 * steps) // 10]],
+        store_us=1000 * sum(store_ms) / steps,
+        bytes_logical=w.algorithmic_bytes(unique=False),
+        bytes_unique=w.algorithmic_bytes(unique=True),
+        flops=w.flops(),
+        wall_s=wall,
+        partitions=-(-w.max_blocks_per_seq * w.block_size // (partition or 512)),
+    )
+    res["decode_GBps"] = res["bytes_logical"] / (res["decode_ms"] * 1e-3) / 1e9
+    res["decode_GBps_unique"] = res["bytes_unique"] / (res["decode_ms"] * 1e-3) / 1e9
+    res["hbm_frac"] = res["decode_GBps_unique"] / HBM_PEAK_GBS
+    del t
+    return res, out
+
+
+def run_prefill(torch, binding, wl, w, steps, warmup, flush, scratch):
+    t = wl.make_device_tensors(w)
+    slots = torch.from_numpy(w.slot_mapping).cuda()
+    cuq = torch.from_numpy(w.cu_seqlens_q).cuda()
+    cuk = torch.from_numpy(w.cu_seqlens_k).cuda()
+    tables = torch.from_numpy(w.block_tables).cuda()
+    out = torch.empty((w.total_q, w.num_q_heads, w.head_dim), dtype=t["q"].dtype, device="cuda")
+
+    def store():
+        binding.pa_store_kvcache(t["k"], t["v"], t["k_cache"], t["v_cache"], slots)
+
+    def pre():
+        binding.pa_prefill_varlen(t["q"], t["k_cache"], t["v_cache"], cuq, cuk, w.max_seqlen_q,
+                                  w.max_seqlen_k, tables, w.scale, out=out)
+
+    for _ in range(warmup):
+        store()
+        pre()
+    torch.cuda.synchronize()
+    timer = Timer(torch, steps, 3)
+    for s in range(steps):
+        if flush:
+            scratch.zero_()
+        timer.rec(s, 0)
+        store()
+        timer.rec(s, 1)
+        pre()
+        timer.rec(s, 2)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out.float()).all()), "prefill: non-finite output"
+    pre_ms = sum(timer.span(1, 2)) / steps
+    store_ms = sum(timer.span(0, 1)) / steps
+    flops = w.flops()
+    res = dict(
+        workload=w.name,
+        prefill_ms=pre_ms,
+        flops=flops,
+        prefill_TFLOPs=flops / (pre_ms * 1e-3) / 1e12,
+        store_us=1000 * store_ms,
+        store_GBps=w.store_bytes() / (store_ms * 1e-3) / 1e9,
+    )
+    res["mfma_frac"] = res["prefill_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
+    del t
+    return res
+
+
+def cpu_baseline(torch, wl, w, seconds):
+    """fp64 oracle on the host over a bounded sample of the decode workload:
+    sequences in order until the time budget is spent."""
+    import numpy as np
+
+    import oracle
+    from tests.helpers import to_host
+
+    t = wl.make_device_tensors(w)
+    bs = w.block_size
+    done_bytes = 0
+    done = 0
+    spent = 0.0
+    for b in range(w.num_seqs):
+        n = int(w.context_lens[b])
+        nb = wl.num_blocks_for(n, bs)
+        ids = torch.from_numpy(w.block_tables[b, :nb].astype(np.int64)).cuda()
+        kh = to_host(t["k_cache"].index_select(0, ids), w.dtype)
+        vh = to_host(t["v_cache"].index_select(0, ids), w.dtype)
+        qh = to_host(t["q"][b:b + 1], w.dtype)
+        nk, nv = to_host(t["k"][b:b + 1], w.dtype), to_host(t["v"][b:b + 1], w.dtype)
+        c0 = time.perf_counter()
+        oracle.store_kvcache(nk, nv, kh, vh, np.array([(nb - 1) * bs + (n - 1) % bs], np.int32))
+        oracle.decode(qh, kh, vh, np.arange(nb, dtype=np.int32)[None], np.array([n], np.int32),
+                      w.scale, w.dtype)
+        spent += time.perf_counter() - c0
+        done += 1
+        done_bytes += n * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes + \
+            2 * w.num_q_heads * w.head_dim * w.elem_bytes + nb * 4 + 4
+        if spent >= seconds:
+            break
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        threads = None
+    del t
+    return {
+        "value": done_bytes / spent / 1e9,
+        "unit": "GB/s",
+        "cores": threads or 1,
+        "kind": "oracle",
+        "sample": f"{done} of {w.num_seqs} sequences of {w.name} (store + decode in fp64 NumPy), "
+                  f"{spent:.1f} s; host has {os.cpu_count()} CPUs",
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from paged_kv_cache_66_amd import binding
+    from paged_kv_cache_66_amd import workloads as wl
+
+    binding.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    flush = not args.no_flush
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if flush else None
+
+    w = wl.qwen3_0p6b_decode(0)
+    log(f"[bench] {w.name}: warmup {args.warmup}, steps {args.steps}")
+    head, _ = run_decode(torch, binding, wl, w, args.steps, args.warmup, flush, scratch, args.partition)
+    log(f"[bench] {w.name}: decode {head['decode_ms'] * 1e3:.1f} us, {head['decode_GBps']:.0f} GB/s")
+
+    secondary = {}
+    if not args.quick:
+        ks = max(5, args.steps // 3)
+        for name, mk in [("8b-decode-bs16", lambda: wl.large_batch_decode(16, 0)),
+                         ("8b-decode-bs256", lambda: wl.large_batch_decode(256, 0)),
+                         ("long-context-decode", lambda: wl.long_context_decode(0))]:
+            log(f"[bench] {name}")
+            r, _ = run_decode(torch, binding, wl, mk(), ks, 2, flush, scratch, args.partition, name)
+            torch.cuda.empty_cache()
+            secondary[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+            log(f"[bench] {name}: decode {r['decode_ms']:.3f} ms, {r['decode_GBps_unique']:.0f} GB/s unique")
+        log("[bench] chunked-prefill")
+        p = run_prefill(torch, binding, wl, wl.chunked_prefill(0), ks, 2, flush, scratch)
+        torch.cuda.empty_cache()
+        secondary["chunked-prefill"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in p.items()}
+        log(f"[bench] prefill {p['prefill_ms']:.3f} ms, {p['prefill_TFLOPs']:.1f} TFLOP/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(torch, wl, w, args.cpu_seconds)
+
+    achieved = head["bytes_logical"] / (head["decode_ms"] * 1e-3) / 1e9
+    value = head["bytes_logical"] / (head["step_ms"] * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) K/V/q on the device; shuffled block pool)",
+        "config": {
+            "workload": w.name,
+            "batch": w.num_seqs,
+            "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim,
+            "block_size": w.block_size,
+            "num_blocks": w.num_blocks,
+            "context_lens": "uniform[128,4096], seed 0",
+            "sum_context": int(w.context_lens.sum()),
+            "step": "pa_store_kvcache(64 new tokens) + pa_decode",
+            "cache": "cold (L2/MALL evicted before each step)" if flush else "warm",
+            "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": stored_traffic(),
+            "kernel": "pa_decode (decode_partition_kernel + decode_reduce_kernel)",
+            "algorithmic_bytes_per_launch": head["bytes_logical"],
+            "avg_launch_ms": round(head["decode_ms"], 5),
+        },
+        "cpu_baseline": cpu,
+        "components": {
+            "decode_ms": round(head["decode_ms"], 5),
+            "decode_ms_p10_p90": [round(x, 5) for x in head["decode_ms_p10_p90"]],
+            "store_us": round(head["store_us"], 2),
+            "partitions": head["partitions"],
+        },
+        "secondary": secondary,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

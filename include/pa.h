@@ -1,0 +1,200 @@
+/*
+ * pa.h - C ABI of the MI355X (gfx950) paged-attention library.
+ *
+ * Three operations make up the data-parallel hot path of a paged KV cache as
+ * the nano-vLLM / vLLM pages describe it:
+ *
+ *   pa_store_kvcache   write this step's new K/V rows into the block pool
+ *                      through slot_mapping;
+ *   pa_decode          one query token per sequence attends over its whole
+ *                      history, gathered through its block-table row (GQA,
+ *                      split-K over token partitions + log-sum-exp merge);
+ *   pa_prefill_varlen  packed variable-length causal prefill whose keys and
+ *                      values (cached prefix + this step's chunk) are read
+ *                      through the block tables.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership.  Every pointer argument is a device pointer owned by the caller
+ *   (typically a torch tensor's data_ptr()). The library allocates no device
+ *   memory and keeps no mutable global state. Work is enqueued
+ *   asynchronously on `stream` (a hipStream_t; NULL = the default stream);
+ *   the caller keeps the buffers alive until the stream has passed them. No
+ *   call reads device memory on the host or synchronises, so every call can
+ *   be captured in a HIP graph.
+ * Layout.  The per-layer caches are k_cache / v_cache of shape
+ *   [num_blocks, block_size, num_kv_heads, head_dim], contiguous ("nano-vLLM
+ *   Part 2: Block Tables, KV Cache, and the Path to the GPU", section 1: the
+ *   per-rank pool [2, L, N, block_size, H_kv, D], one layer's K or V slice).
+ *   A slot is the flattened (block, offset) row index
+ *   block_id * block_size + offset (same page, section 2.2). Row-strided
+ *   q / key / value inputs are views of a fused QKV projection output, so a
+ *   row stride (in elements) is passed; the inner [heads, head_dim] part of a
+ *   row must be contiguous and every row must start on a 16-byte boundary.
+ * Index arrays are int32: slot_mapping, block_tables (padded with -1),
+ *   context_lens, cu_seqlens_q / cu_seqlens_k. All address arithmetic is
+ *   done in 64 bits.
+ * Dtypes.  One element type for q, keys, values, caches and outputs:
+ *   PA_F32 or PA_BF16. Accumulation is always fp32; bf16 outputs are rounded
+ *   to nearest even once at the end.
+ * Errors.  Every problem the host can see (null pointer, bad size,
+ *   unsupported head_dim / block_size / dtype, misalignment, too-small
+ *   workspace) returns a non-zero pa_status and enqueues nothing. A failed
+ *   kernel launch returns PA_ERR_HIP. No C++ exception crosses the ABI.
+ *   Values that live in device memory are trusted preconditions and are NOT
+ *   checked on the device: slots in [-1, num_blocks*block_size) and unique;
+ *   block ids in [0, num_blocks) for the first ceil(len/block_size) table
+ *   entries of each sequence; context_lens[b] <= max_blocks_per_seq *
+ *   block_size; cu_seqlens non-decreasing with 0 <= Lq <= Lk per sequence.
+ * Attention is always causal (the pages call both flash-attn kernels with
+ *   causal=True), so there is no causal flag. Query head h reads kv head
+ *   h / (num_q_heads / num_kv_heads) (contiguous GQA groups).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,       /* a size is negative / zero where it must not be, or inconsistent */
+  PA_ERR_UNSUPPORTED = 3, /* head_dim, block_size, dtype or mode not built */
+  PA_ERR_ALIGN = 4,       /* a pointer or row stride breaks 16-byte alignment */
+  PA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than pa_decode_workspace_size() */
+  PA_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* pa_status_string(int status);
+
+/* Library version string (static). */
+const char* pa_version(void);
+
+/*
+ * pa_store_kvcache - KV scatter ("Inference Engine Inside nano-vLLM",
+ * section "Attention in nano-vLLM": the store kernel launched once per token;
+ * "nano-vLLM Part 2 ...", section 2.3: write K/V of packed token j into
+ * slot_mapping[j]).
+ *
+ * For every t in [0, num_tokens) with s = slot_mapping[t] >= 0:
+ *   k_cache[s / block_size][s % block_size][:][:] = key[t][:][:]
+ *   v_cache[s / block_size][s % block_size][:][:] = value[t][:][:]
+ * bit for bit. A negative slot (the pages use -1, e.g. graph padding rows)
+ * skips the token. Rows not named by slot_mapping are left untouched.
+ *
+ *   key, value        [num_tokens, num_kv_heads, head_dim]; row t starts at
+ *                     key + t * key_row_stride elements (value likewise).
+ *   k_cache, v_cache  [num_blocks, block_size, num_kv_heads, head_dim], written
+ *                     in place.
+ *   slot_mapping      int32 [num_tokens].
+ * num_tokens == 0 is a no-op (pointers other than the caches may be NULL).
+ * head_dim must be 64 or 128; block_size a power of two in [1, 1024].
+ * Slots must be unique; duplicate non-negative slots give an unspecified row.
+ */
+pa_status pa_store_kvcache(const void* key, int64_t key_row_stride,
+                           const void* value, int64_t value_row_stride,
+                           void* k_cache, void* v_cache,
+                           const int32_t* slot_mapping, int32_t num_tokens,
+                           int32_t num_blocks, int32_t block_size,
+                           int32_t num_kv_heads, int32_t head_dim,
+                           pa_dtype dtype, void* stream);
+
+/*
+ * pa_decode_workspace_size - bytes of device workspace pa_decode needs for
+ * these sizes (0 when the call runs as a single pass). partition_size is the
+ * same value later passed to pa_decode (0 = library default).
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                int32_t block_size, int32_t max_blocks_per_seq,
+                                int32_t partition_size);
+
+/*
+ * pa_decode - paged GQA decode attention ("Inference Engine Inside
+ * nano-vLLM", "Attention in nano-vLLM", the flash_attn_with_kvcache branch;
+ * "From nano-vLLM to vLLM ...", section 11.2; "How vLLM Works": the kernel
+ * gathers K and V from scattered physical blocks through the block table).
+ *
+ * For each sequence b with n = context_lens[b] and each query head h
+ * (kv head g = h / (num_q_heads / num_kv_heads)):
+ *   keys/values: logical rows p = 0 .. n-1, row p lives in block
+ *   block_tables[b][p / block_size] at offset p % block_size;
+ *   out[b][h] = softmax(scale * q[b][h] . K_g^T) V_g.
+ * n includes the token being decoded, whose K/V must already be stored (call
+ * pa_store_kvcache first on the same stream). n == 0 writes a zero row and
+ * reads nothing. Table entries at or past ceil(n / block_size) are never
+ * read, so -1 padding and stale ids are harmless.
+ *
+ * The history is cut into partitions of `partition_size` tokens (0 = library
+ * default; otherwise a multiple of 64 up to 4096). When
+ * max_blocks_per_seq * block_size fits one partition the result is written
+ * in one pass; otherwise each partition writes (max, sum, unnormalised
+ * output) partials to `workspace` and a second kernel merges them with the
+ * log-sum-exp rule. The result does not depend on the physical block ids
+ * (bitwise), only on the logical history and the partition size.
+ *
+ *   out           [num_seqs, num_q_heads, head_dim], contiguous.
+ *   q             [num_seqs, num_q_heads, head_dim]; row b at q + b * q_row_stride.
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq], row-major.
+ *   context_lens  int32 [num_seqs].
+ *   workspace     device buffer of >= pa_decode_workspace_size(...) bytes
+ *                 (may be NULL when that size is 0); contents are scratch.
+ * head_dim 64 or 128; num_q_heads a multiple of num_kv_heads with group
+ * size 1, 2, 4, 8 or 16; block_size a power of two in [1, 1024].
+ */
+pa_status pa_decode(void* out, const void* q, int64_t q_row_stride,
+                    const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t num_blocks, float scale,
+                    int32_t partition_size, pa_dtype dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_prefill_varlen - packed varlen causal prefill over a paged cache
+ * ("Inference Engine Inside nano-vLLM", "Attention in nano-vLLM", the
+ * flash_attn_varlen_func branch with k, v = k_cache, v_cache when a prefix
+ * is cached; "nano-vLLM Part 2 ...", sections 2.5 and 4.1; "From nano-vLLM
+ * to vLLM ...", sections 8.1-8.3).
+ *
+ * Sequence i owns query rows cu_seqlens_q[i] .. cu_seqlens_q[i+1]-1
+ * (Lq of them) and sees Lk = cu_seqlens_k[i+1] - cu_seqlens_k[i] keys: the
+ * first Lk logical rows of its block-table row (cached prefix + this step's
+ * chunk, which pa_store_kvcache must have written already). Query j
+ * (0-based within the sequence) sits at position Lk - Lq + j and attends to
+ * keys 0 .. Lk - Lq + j (bottom-right causal alignment):
+ *   out[row][h] = softmax(scale * q[row][h] . K_g[0..Lk-Lq+j]^T) V_g[...].
+ *
+ *   out           [total_q, num_q_heads, head_dim], contiguous.
+ *   q             [total_q, num_q_heads, head_dim]; row r at q + r * q_row_stride.
+ *   cu_seqlens_q, cu_seqlens_k  int32 [num_seqs + 1], device.
+ *   max_seqlen_q  >= every Lq; max_seqlen_k >= every Lk (host integers that
+ *                 size the launch, as the pages pass them).
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq]. NULL (packed
+ *                 contiguous K/V mode) is not built yet: PA_ERR_UNSUPPORTED.
+ * Only PA_BF16 is built (the contractions run on bf16 MFMA with fp32
+ * accumulation); head_dim 64 or 128; group size 1, 2, 4, 8 or 16; block_size
+ * a power of two in [16, 1024].
+ */
+pa_status pa_prefill_varlen(void* out, const void* q, int64_t q_row_stride, int32_t total_q,
+                            const void* k_cache, const void* v_cache,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            int32_t max_seqlen_q, int32_t max_seqlen_k,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            float scale, pa_dtype dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,197 @@
+"""Thin Python binding over the C ABI in ``libpa.so`` (see include/pa.h).
+
+Argument marshalling only: tensors are checked for device, dtype and shape,
+their data pointers and the current torch stream are handed to the C entry
+point of the same name, and a non-zero status raises :class:`PaError`. Every
+step of the computation runs in the HIP kernels; there is no fallback. If the
+library is missing the first call raises instead of computing anything.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpa.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "pa.h")
+
+PA_F32, PA_BF16 = 0, 1
+STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
+          4: "PA_ERR_ALIGN", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP"}
+
+
+class PaError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+_lib = None
+
+_i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+_SIGNATURES = {
+    "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_version": (ctypes.c_char_p, []),
+    "pa_store_kvcache": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                        _i32, ctypes.c_int, _vp]),
+    "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                 _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _sz, _vp]),
+    "pa_prefill_varlen": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
+                                         _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                         ctypes.c_int, _vp]),
+}
+
+
+def header_symbols(path: str = HEADER) -> list[str]:
+    """Names of the functions include/pa.h declares."""
+    with open(path) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\*?\s+\*?(pa_\w+)\s*\(", text, re.M)))
+
+
+def load(path: str = LIB_PATH):
+    """Load (once) and return the ctypes handle of libpa.so."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library not built: {path} is missing "
+                           "(run python -m paged_kv_cache_66_amd.build)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        msg = load().pa_status_string(status).decode()
+        raise PaError(fn, status, msg)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(t):
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _require(cond: bool, what: str):
+    if not cond:
+        raise ValueError(what)
+
+
+def _rows(t, name: str):
+    """(pointer, row stride in elements) of a [T, heads, head_dim] tensor
+    whose inner two dimensions are contiguous."""
+    _require(t.dim() == 3, f"{name} must be 3-D")
+    _require(t.stride(2) == 1 and t.stride(1) == t.shape[2], f"{name}: inner dims must be contiguous")
+    return t.data_ptr(), t.stride(0)
+
+
+def _int32(t, name):
+    import torch
+    _require(t.dtype == torch.int32, f"{name} must be int32")
+    _require(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _cache_dims(k_cache, v_cache):
+    _require(k_cache.dim() == 4 and k_cache.is_contiguous(), "k_cache must be contiguous [N, bs, H_kv, D]")
+    _require(v_cache.shape == k_cache.shape and v_cache.is_contiguous(), "v_cache must match k_cache")
+    _require(v_cache.dtype == k_cache.dtype, "k_cache and v_cache dtypes differ")
+    return tuple(int(x) for x in k_cache.shape)
+
+
+def pa_store_kvcache(key, value, k_cache, v_cache, slot_mapping) -> None:
+    """Scatter key/value rows [T, H_kv, D] into the caches at slot_mapping."""
+    lib = load()
+    n, bs, hkv, d = _cache_dims(k_cache, v_cache)
+    _int32(slot_mapping, "slot_mapping")
+    t = int(slot_mapping.shape[0])
+    kp, ks = _rows(key, "key")
+    vp, vs = _rows(value, "value")
+    _require(key.shape[0] == t and value.shape[0] == t, "key/value rows != len(slot_mapping)")
+    _require(tuple(key.shape[1:]) == (hkv, d) and tuple(value.shape[1:]) == (hkv, d), "key/value head shape")
+    _require(key.dtype == k_cache.dtype == value.dtype, "dtype mismatch")
+    st = lib.pa_store_kvcache(kp, ks, vp, vs, k_cache.data_ptr(), v_cache.data_ptr(),
+                              slot_mapping.data_ptr(), t, n, bs, hkv, d, _dtype_code(k_cache),
+                              _stream(k_cache))
+    _check("pa_store_kvcache", st)
+
+
+def pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, block_size, max_blocks_per_seq,
+                             partition_size=0) -> int:
+    return int(load().pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, block_size,
+                                                max_blocks_per_seq, partition_size))
+
+
+def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None, workspace=None,
+              partition_size=0):
+    """Paged GQA decode. q [B, H_q, D]; returns out [B, H_q, D]."""
+    import torch
+    lib = load()
+    n, bs, hkv, d = _cache_dims(k_cache, v_cache)
+    _int32(block_tables, "block_tables")
+    _int32(context_lens, "context_lens")
+    qp, qs = _rows(q, "q")
+    b, hq = int(q.shape[0]), int(q.shape[1])
+    _require(q.shape[2] == d and q.dtype == k_cache.dtype, "q shape/dtype")
+    _require(block_tables.dim() == 2 and block_tables.shape[0] == b, "block_tables must be [B, W]")
+    _require(context_lens.shape == (b,), "context_lens must be [B]")
+    w = int(block_tables.shape[1])
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=q.dtype, device=q.device)
+    _require(out.is_contiguous() and tuple(out.shape) == (b, hq, d) and out.dtype == q.dtype, "out")
+    need = pa_decode_workspace_size(b, hq, d, bs, w, partition_size) if b > 0 else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wp = workspace.data_ptr() if workspace is not None else None
+    wn = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.pa_decode(out.data_ptr(), qp, qs, k_cache.data_ptr(), v_cache.data_ptr(),
+                       block_tables.data_ptr(), w, context_lens.data_ptr(), b, hq, hkv, d, bs, n,
+                       float(scale), int(partition_size), _dtype_code(q), wp, wn, _stream(q))
+    _check("pa_decode", st)
+    return out
+
+
+def pa_prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                      block_tables, scale, out=None):
+    """Packed varlen causal prefill through the block tables. q [Tq, H_q, D]."""
+    import torch
+    lib = load()
+    n, bs, hkv, d = _cache_dims(k_cache, v_cache)
+    _int32(cu_seqlens_q, "cu_seqlens_q")
+    _int32(cu_seqlens_k, "cu_seqlens_k")
+    qp, qs = _rows(q, "q")
+    tq, hq = int(q.shape[0]), int(q.shape[1])
+    _require(q.shape[2] == d and q.dtype == k_cache.dtype, "q shape/dtype")
+    bsq = int(cu_seqlens_q.shape[0]) - 1
+    _require(cu_seqlens_k.shape == cu_seqlens_q.shape, "cu_seqlens_k must match cu_seqlens_q")
+    if block_tables is not None:
+        _int32(block_tables, "block_tables")
+        _require(block_tables.dim() == 2 and block_tables.shape[0] == bsq, "block_tables must be [B, W]")
+        bt_ptr, w = block_tables.data_ptr(), int(block_tables.shape[1])
+    else:
+        bt_ptr, w = None, 0
+    if out is None:
+        out = torch.empty((tq, hq, d), dtype=q.dtype, device=q.device)
+    _require(out.is_contiguous() and tuple(out.shape) == (tq, hq, d) and out.dtype == q.dtype, "out")
+    st = lib.pa_prefill_varlen(out.data_ptr(), qp, qs, tq, k_cache.data_ptr(), v_cache.data_ptr(),
+                               cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), int(max_seqlen_q),
+                               int(max_seqlen_k), bt_ptr, w, bsq, hq, hkv, d, bs, n, float(scale),
+                               _dtype_code(q), _stream(q))
+    _check("pa_prefill_varlen", st)
+    return out

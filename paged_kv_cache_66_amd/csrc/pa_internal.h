@@ -1,0 +1,75 @@
+// Internal launcher interface between the C ABI (pa_api.cpp) and the HIP
+// kernels. All arguments have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct StoreArgs {
+  const void* key;
+  int64_t key_stride_bytes;
+  const void* value;
+  int64_t value_stride_bytes;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* slot_mapping;
+  int32_t num_tokens;
+  int32_t row_bytes;  // num_kv_heads * head_dim * element bytes
+};
+
+hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  int64_t q_stride;  // elements
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  float scale;
+  int32_t partition;     // tokens per partition
+  int32_t num_partitions;  // max partitions per sequence (grid x)
+  float* ws_acc;         // [B, H_q, P, D] when num_partitions > 1
+  float* ws_ml;          // [B, H_q, P, 2]
+  bool bf16;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  int64_t q_stride;  // elements
+  int32_t total_q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int32_t max_seqlen_q;
+  int32_t max_seqlen_k;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  float scale;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// Partition sizing shared by pa_decode and pa_decode_workspace_size.
+int32_t decode_partition_tokens(int32_t requested, int32_t block_size, int32_t max_blocks);
+
+}  // namespace pa

@@ -1,0 +1,319 @@
+// Packed varlen causal prefill over a paged KV cache, on bf16 MFMA.
+//
+// What is computed ("Inference Engine Inside nano-vLLM", "Attention in
+// nano-vLLM", flash_attn_varlen_func with k, v = k_cache, v_cache and the
+// block table; "nano-vLLM Part 2 ...", sections 2.5 and 4.1): sequence i has
+// Lq query rows packed at cu_seqlens_q[i] and Lk visible keys; query j sits
+// at position Lk - Lq + j and attends to keys 0 .. Lk - Lq + j, all read
+// through the sequence's block-table row.
+//
+// Design (CDNA4 / gfx950): FlashAttention-style tiling (the pages' note that
+// the kernels tile Q, K and V through on-chip memory while the cache stays
+// in HBM, "nano-vLLM Part 2 ...", section 1.2), written for 64-wide waves and
+// the v_mfma_f32_16x16x32_bf16 matrix instruction:
+// * a workgroup owns 128 (query head, query) rows of one kv head: the G
+//   query heads that share the kv head are packed together, so every K/V
+//   tile staged in LDS serves 128 rows whatever G is;
+// * per 64-key tile the scores are formed transposed, S^T = K Q^T (K rows
+//   from LDS as the A operand, Q slices held in registers as the B operand),
+//   so each lane ends up with four consecutive keys of one query column;
+//   softmax statistics then need only two cross-lane steps per column;
+// * O^T = V^T P^T: the B operand P^T is assembled in registers straight from
+//   the score accumulators (the contraction index is permuted identically on
+//   both operands), and V is written to LDS transposed ([d][key]) so the A
+//   operand is two 8-byte LDS reads;
+// * online softmax in the log2 domain; only the tiles that cross the causal
+//   diagonal or the end of the keys are masked;
+// * the next tile's K/V rows are fetched into registers while the current
+//   tile is being multiplied.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kRows = 128;  // (head, query) rows per workgroup
+constexpr int kKeys = 64;   // keys per tile
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const Vec16& v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ uint32_t half16(const Vec16& v, int j) {
+  const uint32_t w = v.w[j >> 1];
+  return (j & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
+    uint16_t* __restrict__ out, const char* __restrict__ q, int64_t q_stride_bytes,
+    const char* __restrict__ k_cache, const char* __restrict__ v_cache,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+    const int32_t* __restrict__ block_tables, int32_t max_blocks, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t log2_bs, float scale_log2) {
+  constexpr int QT = kRows / G;    // queries per workgroup
+  constexpr int KS = D / 32;       // MFMA k-steps over head_dim
+  constexpr int DT = D / 16;       // 16-wide head_dim tiles of the output
+  constexpr int KPITCH = D + 8;    // bf16 per K row in LDS (padding spreads banks)
+  constexpr int VPITCH = kKeys + 4;  // bf16 per transposed V row in LDS
+  constexpr int KCH = D / 8;       // 16-byte chunks per K row
+  constexpr int KLOADS = kKeys * KCH / kThreads;  // K vectors per thread per tile
+  constexpr int VITEMS = (kKeys / 4) * KCH;       // (4-key group, chunk) items per tile
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kKeys * KPITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[D * VPITCH];
+
+  const int i = blockIdx.z;
+  const int g = blockIdx.y;
+  const int q0 = cu_q[i];
+  const int Lq = cu_q[i + 1] - q0;
+  const int Lk = cu_k[i + 1] - cu_k[i];
+  const int n_qt = (Lq + QT - 1) / QT;
+  if (static_cast<int>(blockIdx.x) >= n_qt) return;
+  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x);  // heaviest tiles first
+  const int q_lo = qt * QT;
+  const int q_hi = min(q_lo + QT, Lq);
+  const int start = Lk - Lq;
+  const int kmax = min(Lk, start + q_hi);
+  const int nkt = (kmax + kKeys - 1) / kKeys;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15;  // MFMA column / row-in-operand index
+  const int gq = lane >> 4;   // MFMA lane group
+
+  // ---- Q operands (B of S^T = K Q^T), positions and output rows ----
+  bf16x8_t qop[2][KS];
+  int posq[2];
+  int orow[2];   // packed query row, -1 when this column is padding
+  int ohead[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int r = wave * 32 + t * 16 + col;
+    const int hl = r / QT;
+    const int ql = r % QT;
+    const int qi = q_lo + ql;
+    const int head = g * G + hl;
+    posq[t] = start + qi;
+    orow[t] = qi < Lq ? q0 + qi : -1;
+    ohead[t] = head;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      Vec16 v{{0u, 0u, 0u, 0u}};
+      if (qi < Lq) {
+        v = load16(q + static_cast<int64_t>(q0 + qi) * q_stride_bytes +
+                   (static_cast<int64_t>(head) * D + ks * 32 + gq * 8) * 2);
+      }
+      qop[t][ks] = as_bf16x8(v);
+    }
+  }
+
+  const int64_t row_bytes = static_cast<int64_t>(num_kv_heads) * D * 2;
+  const int64_t head_off = static_cast<int64_t>(g) * D * 2;
+  const int32_t* table = block_tables + static_cast<int64_t>(i) * max_blocks;
+  const int bs_mask = (1 << log2_bs) - 1;
+
+  auto row_addr = [&](int key) -> int64_t {
+    const int64_t blk = table[key >> log2_bs];
+    return ((blk << log2_bs) + (key & bs_mask)) * row_bytes + head_off;
+  };
+
+  // ---- tile fetch into registers ----
+  Vec16 kreg[KLOADS];
+  Vec16 vreg[4];
+  const int vkg = tid % (kKeys / 4);  // 4-key group of the V item
+  const int vdc = tid / (kKeys / 4);  // 16-byte chunk of the V item
+  auto fetch = [&](int kt0) {
+#pragma unroll
+    for (int u = 0; u < KLOADS; ++u) {
+      const int item = tid + u * kThreads;
+      const int r = item / KCH;
+      const int c = item % KCH;
+      const int key = kt0 + r;
+      kreg[u] = key < Lk ? load16(k_cache + row_addr(key) + c * 16) : Vec16{{0u, 0u, 0u, 0u}};
+    }
+    if (tid < VITEMS) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = kt0 + vkg * 4 + e;
+        vreg[e] = key < Lk ? load16(v_cache + row_addr(key) + vdc * 16) : Vec16{{0u, 0u, 0u, 0u}};
+      }
+    }
+  };
+  auto commit = [&]() {
+#pragma unroll
+    for (int u = 0; u < KLOADS; ++u) {
+      const int item = tid + u * kThreads;
+      const int r = item / KCH;
+      const int c = item % KCH;
+      *reinterpret_cast<Vec16*>(&sK[r * KPITCH + c * 8]) = kreg[u];
+    }
+    if (tid < VITEMS) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int d = vdc * 8 + j;
+        uint2 pk;
+        pk.x = half16(vreg[0], j) | (half16(vreg[1], j) << 16);
+        pk.y = half16(vreg[2], j) | (half16(vreg[3], j) << 16);
+        *reinterpret_cast<uint2*>(&sV[d * VPITCH + vkg * 4]) = pk;
+      }
+    }
+  };
+
+  f32x4_t o[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) o[dt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY};
+  float l[2] = {0.f, 0.f};
+
+  if (nkt > 0) fetch(0);
+  for (int j = 0; j < nkt; ++j) {
+    const int kt0 = j * kKeys;
+    __syncthreads();  // previous tile fully consumed
+    commit();
+    __syncthreads();
+    if (j + 1 < nkt) fetch(kt0 + kKeys);
+
+    // S^T tile: 64 keys x 32 (head, query) columns per wave
+    f32x4_t s[4][2];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) s[kt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const Vec16 kv = *reinterpret_cast<const Vec16*>(&sK[(kt * 16 + col) * KPITCH + ks * 32 + gq * 8]);
+        const bf16x8_t ka = as_bf16x8(kv);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          s[kt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qop[t][ks], s[kt][t], 0, 0, 0);
+      }
+    }
+
+    const bool need_mask = !(kt0 + kKeys - 1 <= start + q_lo && kt0 + kKeys <= Lk);
+    uint32_t pop[2][2][4];  // [k-step of 32 keys][t][packed pair]
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v = s[kt][t][e] * scale_log2;
+          if (need_mask) {
+            const int key = kt0 + kt * 16 + gq * 4 + e;
+            if (key > posq[t] || key >= Lk) v = -INFINITY;
+          }
+          s[kt][t][e] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float m_new = fmaxf(m[t], tmax);
+      const float alpha = exp2f(m[t] - m_new);
+      m[t] = m_new;
+      float lsum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = exp2f(s[kt][t][e] - m_new);
+          s[kt][t][e] = p;
+          lsum += p;
+        }
+      l[t] = l[t] * alpha + lsum;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt][t] *= alpha;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        pop[st][t][0] = pack_bf16x2(s[2 * st][t][0], s[2 * st][t][1]);
+        pop[st][t][1] = pack_bf16x2(s[2 * st][t][2], s[2 * st][t][3]);
+        pop[st][t][2] = pack_bf16x2(s[2 * st + 1][t][0], s[2 * st + 1][t][1]);
+        pop[st][t][3] = pack_bf16x2(s[2 * st + 1][t][2], s[2 * st + 1][t][3]);
+      }
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const uint16_t* vrow = &sV[(dt * 16 + col) * VPITCH + st * 32 + gq * 4];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+        const Vec16 va{{lo.x, lo.y, hi.x, hi.y}};
+        const bf16x8_t a = as_bf16x8(va);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const Vec16 pb{{pop[st][t][0], pop[st][t][1], pop[st][t][2], pop[st][t][3]}};
+          o[dt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pb), o[dt][t], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- normalise and write ----
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    float lt = l[t];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    if (orow[t] < 0) continue;
+    const float inv = 1.f / lt;
+    uint16_t* orow_ptr = out + (static_cast<int64_t>(orow[t]) * num_q_heads + ohead[t]) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      uint2 w;
+      w.x = pack_bf16x2(o[dt][t][0] * inv, o[dt][t][1] * inv);
+      w.y = pack_bf16x2(o[dt][t][2] * inv, o[dt][t][3] * inv);
+      *reinterpret_cast<uint2*>(orow_ptr + dt * 16 + gq * 4) = w;
+    }
+  }
+}
+
+template <int D, int G>
+hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
+  constexpr int QT = kRows / G;
+  int log2_bs = 0;
+  while ((1 << log2_bs) < a.block_size) ++log2_bs;
+  const int max_qt = (a.max_seqlen_q + QT - 1) / QT;
+  if (max_qt == 0 || a.num_seqs == 0) return hipSuccess;
+  dim3 grid(max_qt, a.num_kv_heads, a.num_seqs);
+  hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(kThreads), 0, stream,
+                     static_cast<uint16_t*>(a.out), static_cast<const char*>(a.q), a.q_stride * 2,
+                     static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache), a.cu_q,
+                     a.cu_k, a.block_tables, a.max_blocks, a.num_q_heads, a.num_kv_heads, log2_bs,
+                     a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t dispatch_prefill_group(const PrefillArgs& a, hipStream_t stream) {
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_prefill_typed<D, 1>(a, stream);
+    case 2: return launch_prefill_typed<D, 2>(a, stream);
+    case 4: return launch_prefill_typed<D, 4>(a, stream);
+    case 8: return launch_prefill_typed<D, 8>(a, stream);
+    case 16: return launch_prefill_typed<D, 16>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  return a.head_dim == 64 ? dispatch_prefill_group<64>(a, stream)
+                          : dispatch_prefill_group<128>(a, stream);
+}
+
+}  // namespace pa

@@ -1,0 +1,137 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+include/pa.h declares, and rejects bad arguments with the documented status
+codes before touching the GPU (no kernel is ever launched here)."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from paged_kv_cache_66_amd import binding
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS = 0, 1, 2, 3, 4, 5
+F32, BF16 = 0, 1
+A = 1 << 20  # a 16-byte aligned fake device address: never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from paged_kv_cache_66_amd import build
+        build.build()
+    return binding.load()
+
+
+def test_exports_every_header_symbol(lib):
+    names = binding.header_symbols()
+    assert set(names) == {"pa_status_string", "pa_version", "pa_store_kvcache",
+                          "pa_decode_workspace_size", "pa_decode", "pa_prefill_varlen"}
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.pa_status_string(s)
+    assert b"unknown" in lib.pa_status_string(99)
+    assert b"gfx950" in lib.pa_version()
+
+
+def store(lib, **kw):
+    a = dict(key=A, ks=128, value=A, vs=128, kc=A, vc=A, slots=A, t=4, n=32, bs=16, hkv=2, d=64,
+             dtype=F32)
+    a.update(kw)
+    return lib.pa_store_kvcache(a["key"], a["ks"], a["value"], a["vs"], a["kc"], a["vc"], a["slots"],
+                                a["t"], a["n"], a["bs"], a["hkv"], a["d"], a["dtype"], None)
+
+
+def test_store_validation(lib):
+    assert store(lib, t=0, key=None, value=None, slots=None) == OK  # no-op
+    assert store(lib, kc=None) == NULL
+    assert store(lib, slots=None) == NULL
+    assert store(lib, t=-1) == SHAPE
+    assert store(lib, d=96) == UNSUP
+    assert store(lib, bs=24) == UNSUP
+    assert store(lib, bs=2048) == UNSUP
+    assert store(lib, dtype=7) == UNSUP
+    assert store(lib, n=0) == SHAPE
+    assert store(lib, ks=100) == SHAPE          # stride shorter than a row
+    assert store(lib, ks=130) == ALIGN          # 520-byte rows are not 16-byte multiples
+    assert store(lib, key=A + 4) == ALIGN
+    assert store(lib, kc=A + 8) == ALIGN
+    assert store(lib, n=1 << 28, bs=1024) == SHAPE  # slots would overflow int32
+
+
+def decode(lib, **kw):
+    a = dict(out=A, q=A, qs=256, kc=A, vc=A, bt=A, w=4, ctx=A, b=4, hq=4, hkv=2, d=64, bs=16, n=32,
+             scale=0.125, part=0, dtype=F32, ws=None, wsn=0)
+    a.update(kw)
+    return lib.pa_decode(a["out"], a["q"], a["qs"], a["kc"], a["vc"], a["bt"], a["w"], a["ctx"], a["b"],
+                         a["hq"], a["hkv"], a["d"], a["bs"], a["n"], a["scale"], a["part"], a["dtype"],
+                         a["ws"], a["wsn"], None)
+
+
+def test_decode_validation(lib):
+    assert decode(lib, b=0, out=None, q=None) == OK
+    assert decode(lib, out=None) == NULL
+    assert decode(lib, bt=None) == NULL
+    assert decode(lib, hq=3) == SHAPE
+    assert decode(lib, hq=6, hkv=2) == UNSUP     # group size 3
+    assert decode(lib, hq=64, hkv=2) == UNSUP    # group size 32
+    assert decode(lib, d=80) == UNSUP
+    assert decode(lib, bs=12) == UNSUP
+    assert decode(lib, w=0) == SHAPE
+    assert decode(lib, qs=100) == SHAPE
+    assert decode(lib, q=A + 4) == ALIGN
+    assert decode(lib, part=100) == UNSUP
+    assert decode(lib, part=8192) == UNSUP
+    assert decode(lib, part=4096, hq=16, hkv=2) == UNSUP  # 8 * 4096 scores exceed LDS
+    assert decode(lib, scale=float("inf")) == SHAPE
+    # W * bs = 64 > partition 0 -> default 512: single pass, no workspace needed
+    assert lib.pa_decode_workspace_size(4, 4, 64, 16, 4, 0) == 0
+    # W * bs = 2048 -> 4 partitions of 512: workspace required
+    need = lib.pa_decode_workspace_size(4, 4, 64, 16, 128, 0)
+    assert need == 4 * 4 * 4 * (64 + 2) * 4
+    assert decode(lib, w=128) == WS
+    assert decode(lib, w=128, ws=A, wsn=need - 1) == WS
+    assert decode(lib, w=128, ws=A + 4, wsn=need) == ALIGN
+    assert lib.pa_decode_workspace_size(4, 4, 64, 16, 4, 64) == 4 * 4 * 1 * (64 + 2) * 4 or \
+        lib.pa_decode_workspace_size(4, 4, 64, 16, 4, 64) == 0
+
+
+def prefill(lib, **kw):
+    a = dict(out=A, q=A, qs=512, tq=8, kc=A, vc=A, cuq=A, cuk=A, mq=8, mk=8, bt=A, w=4, b=1, hq=4,
+             hkv=2, d=128, bs=16, n=32, scale=0.1, dtype=BF16)
+    a.update(kw)
+    return lib.pa_prefill_varlen(a["out"], a["q"], a["qs"], a["tq"], a["kc"], a["vc"], a["cuq"],
+                                 a["cuk"], a["mq"], a["mk"], a["bt"], a["w"], a["b"], a["hq"], a["hkv"],
+                                 a["d"], a["bs"], a["n"], a["scale"], a["dtype"], None)
+
+
+def test_prefill_validation(lib):
+    assert prefill(lib, b=0) == OK
+    assert prefill(lib, tq=0) == OK
+    assert prefill(lib, dtype=F32) == UNSUP      # only bf16 MFMA path is built
+    assert prefill(lib, bt=None) == UNSUP        # packed contiguous mode not built yet
+    assert prefill(lib, cuq=None) == NULL
+    assert prefill(lib, hq=5) == SHAPE
+    assert prefill(lib, d=32) == UNSUP
+    assert prefill(lib, qs=256) == SHAPE
+    assert prefill(lib, out=A + 2) == ALIGN
+    assert prefill(lib, mq=-1) == SHAPE
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import importlib
+    mod = importlib.import_module("paged_kv_cache_66_amd.binding")
+    saved = mod._lib
+    try:
+        mod._lib = None
+        with pytest.raises(RuntimeError, match="not built"):
+            mod.load(str(tmp_path / "missing.so"))
+    finally:
+        mod._lib = saved
