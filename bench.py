@@ -6,8 +6,9 @@ step -- 64 sequences, H_q=16, H_kv=8, D=128, bf16, block size 256, a shuffled
 pool of 4096 blocks, context lengths uniform in [128, 4096]. One step is
 pa_store_kvcache of the 64 new tokens followed by pa_decode over every
 sequence's whole history. Inputs are generated on the device (seed 0) before
-timing; an untimed 1 GiB write evicts L2/MALL before each step so every step
-reads its KV cold, as a layer's KV would be in a real model step.
+timing; an untimed read of a 1 GiB buffer evicts L2/MALL before each step so
+every step reads its KV cold, as a layer's KV would be in a real model step
+(a read, not a write, so no dirty lines are left for the step to write back).
 
 Also measured in the same run (unless --quick): the chunked varlen prefill
 workload (16384 query tokens over 24 sequences with shared cached prefixes:
@@ -75,6 +76,11 @@ def stored_traffic():
     return rec.get("bytes_per_launch")
 
 
+def flush_caches(scratch):
+    """Evict L2 and MALL by streaming a 1 GiB buffer through them (reads)."""
+    scratch.view(-1).amax()
+
+
 class Timer:
     """Per-step HIP events on the current stream."""
 
@@ -95,8 +101,8 @@ def run_decode(torch, binding, wl, w, steps, warmup, flush, scratch, partition=0
     tables = torch.from_numpy(w.block_tables).cuda()
     ctx = torch.from_numpy(w.context_lens).cuda()
     out = torch.empty_like(t["q"].contiguous())
-    need = binding.pa_decode_workspace_size(w.num_seqs, w.num_q_heads, w.head_dim, w.block_size,
-                                            w.max_blocks_per_seq, partition)
+    need = binding.pa_decode_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                            w.block_size, w.max_blocks_per_seq, partition)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
 
     def step():
@@ -115,7 +121,7 @@ def run_decode(torch, binding, wl, w, steps, warmup, flush, scratch, partition=0
     t0 = time.perf_counter()
     for s in range(steps):
         if flush:
-            scratch.zero_()
+            flush_caches(scratch)
         timer.rec(s, 0)
         step()
         timer.rec(s, 1)
@@ -137,7 +143,6 @@ def run_decode(torch, binding, wl, w, steps, warmup, flush, scratch, partition=0
         bytes_unique=w.algorithmic_bytes(unique=True),
         flops=w.flops(),
         wall_s=wall,
-        partitions=-(-w.max_blocks_per_seq * w.block_size // (partition or 512)),
     )
     res["decode_GBps"] = res["bytes_logical"] / (res["decode_ms"] * 1e-3) / 1e9
     res["decode_GBps_unique"] = res["bytes_unique"] / (res["decode_ms"] * 1e-3) / 1e9
@@ -168,7 +173,7 @@ def run_prefill(torch, binding, wl, w, steps, warmup, flush, scratch):
     timer = Timer(torch, steps, 3)
     for s in range(steps):
         if flush:
-            scratch.zero_()
+            flush_caches(scratch)
         timer.rec(s, 0)
         store()
         timer.rec(s, 1)
@@ -255,7 +260,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     flush = not args.no_flush
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if flush else None
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda") if flush else None
 
     w = wl.qwen3_0p6b_decode(0)
     log(f"[bench] {w.name}: warmup {args.warmup}, steps {args.steps}")
@@ -329,7 +334,6 @@ def main():
             "decode_ms": round(head["decode_ms"], 5),
             "decode_ms_p10_p90": [round(x, 5) for x in head["decode_ms_p10_p90"]],
             "store_us": round(head["store_us"], 2),
-            "partitions": head["partitions"],
         },
         "secondary": secondary,
     }

@@ -109,11 +109,12 @@ pa_status pa_store_kvcache(const void* key, int64_t key_row_stride,
 
 /*
  * pa_decode_workspace_size - bytes of device workspace pa_decode needs for
- * these sizes (0 when the call runs as a single pass). partition_size is the
- * same value later passed to pa_decode (0 = library default).
+ * these sizes (0 when the call runs as a single pass, or when the sizes are
+ * invalid). partition_size is the same value later passed to pa_decode
+ * (0 = library default, which depends on the launch shape).
  */
-size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                int32_t block_size, int32_t max_blocks_per_seq,
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                 int32_t partition_size);
 
 /*
@@ -133,7 +134,8 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
  * read, so -1 padding and stale ids are harmless.
  *
  * The history is cut into partitions of `partition_size` tokens (0 = library
- * default; otherwise a multiple of 64 up to 4096). When
+ * default; otherwise a multiple of 64 up to 4096 with
+ * (num_q_heads / num_kv_heads) * partition_size <= 8192). When
  * max_blocks_per_seq * block_size fits one partition the result is written
  * in one pass; otherwise each partition writes (max, sum, unnormalised
  * output) partials to `workspace` and a second kernel merges them with the

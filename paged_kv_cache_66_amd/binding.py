@@ -36,7 +36,7 @@ _SIGNATURES = {
     "pa_version": (ctypes.c_char_p, []),
     "pa_store_kvcache": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                         _i32, ctypes.c_int, _vp]),
-    "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                  _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _sz, _vp]),
     "pa_prefill_varlen": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
@@ -132,10 +132,10 @@ def pa_store_kvcache(key, value, k_cache, v_cache, slot_mapping) -> None:
     _check("pa_store_kvcache", st)
 
 
-def pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, block_size, max_blocks_per_seq,
-                             partition_size=0) -> int:
-    return int(load().pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, block_size,
-                                                max_blocks_per_seq, partition_size))
+def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                             max_blocks_per_seq, partition_size=0) -> int:
+    return int(load().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                block_size, max_blocks_per_seq, partition_size))
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None, workspace=None,
@@ -155,7 +155,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None, 
     if out is None:
         out = torch.empty((b, hq, d), dtype=q.dtype, device=q.device)
     _require(out.is_contiguous() and tuple(out.shape) == (b, hq, d) and out.dtype == q.dtype, "out")
-    need = pa_decode_workspace_size(b, hq, d, bs, w, partition_size) if b > 0 else 0
+    need = pa_decode_workspace_size(b, hq, hkv, d, bs, w, partition_size) if b > 0 else 0
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wp = workspace.data_ptr() if workspace is not None else None

@@ -8,17 +8,19 @@
 // table[p / block_size] at offset p % block_size).
 //
 // Work decomposition (MI355X): one 256-thread workgroup per (partition of
-// `partition` tokens, kv head, sequence). The G = H_q / H_kv query heads of
-// a kv head are handled together, so each K/V row is read from HBM once per
-// kv head and applied to all G heads from registers.
+// `partition` tokens, kv head, sequence), kv head fastest in dispatch order
+// so the workgroups that read the head slices of the same token rows run
+// side by side. The G = H_q / H_kv query heads of a kv head are handled
+// together, so each K/V row is read from HBM once per kv head and applied to
+// all G heads from registers.
 //   phase 0  the partition's block ids are staged in LDS (one coalesced load
 //            instead of a dependent table read per row);
 //   phase 1  K rows stream in as 16-byte vectors: a row of one kv head
 //            (head_dim elements) is spread over LPT lanes, a wave covers
 //            64 / LPT rows per load; each lane dots its slice against the G
-//            query slices held in registers and the LPT partial sums are
-//            combined with cross-lane shuffles; scores (already scaled by
-//            scale * log2 e) go to LDS, token-major;
+//            query slices held in registers (v_dot2_f32_bf16 on bf16) and
+//            the LPT partial sums are combined with DPP row operations;
+//            scores (scaled by scale * log2 e) go to LDS, token-major;
 //   phase 2  exact per-head max and sum of exp2(s - max) over the partition
 //            (no running rescale is needed because all scores are known);
 //   phase 3  V rows stream in the same way; each lane accumulates
@@ -41,10 +43,30 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 8;
 
+// DPP lane patterns (gfx9 encoding): quad permutations and row mirrors.
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of LPT consecutive lanes; every lane of a group
+// receives the group's sum. Within a 16-lane row the steps are DPP moves
+// folded into the adds (quad swaps, then the half-row and row mirrors, each
+// of which pairs a lane with one in the other half of its current group);
+// only a 32-lane group needs a cross-row exchange.
 template <int LPT>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int off = LPT / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  static_assert(LPT == 8 || LPT == 16 || LPT == 32, "lanes per row");
+  v = dpp_add<kDppQuadXor1>(v);
+  v = dpp_add<kDppQuadXor2>(v);
+  v = dpp_add<kDppRowHalfMirror>(v);
+  if constexpr (LPT >= 16) v = dpp_add<kDppRowMirror>(v);
+  if constexpr (LPT == 32) v += __shfl_xor(v, 16, 64);
   return v;
 }
 
@@ -59,6 +81,43 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
+
+// Query slice of one head held by a lane, in the form the score dot product
+// wants: fp32 values for fp32 caches, raw bf16 pairs for bf16 caches (the
+// products of two bf16 values are exact in fp32, so v_dot2_f32_bf16 computes
+// the same partial sums as widening first, with no conversion instructions).
+template <typename T> struct QSlice;
+
+template <> struct QSlice<float> {
+  float v[4];
+  __device__ __forceinline__ void load(const Vec16& x) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(x.w[e]);
+  }
+  __device__ __forceinline__ float dot(const Vec16& k) const {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fmaf(v[e], __uint_as_float(k.w[e]), acc);
+    return acc;
+  }
+};
+
+template <> struct QSlice<BF16Tag> {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  uint32_t v[4];
+  __device__ __forceinline__ void load(const Vec16& x) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) v[w] = x.w[w];
+  }
+  __device__ __forceinline__ float dot(const Vec16& k) const {
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v[w]),
+                                            __builtin_bit_cast(bf16x2_t, k.w[w]), acc, false);
+    return acc;
+  }
+};
 
 // Dynamic LDS layout of the partition kernel (in 4-byte words):
 //   [0, G * max(partition, 4 * D))   scores, then reused for the wave reduction
@@ -84,9 +143,11 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   float* s_sum = s_max + G;                               // [G]
   int32_t* s_ids = reinterpret_cast<int32_t*>(s_sum + G);  // block ids of the partition
 
-  const int p = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+  // The kv heads of one partition are adjacent in dispatch order, so the
+  // workgroups reading the slices of the same token rows run together.
+  const int g = static_cast<int>(blockIdx.x) % num_kv_heads;
+  const int p = static_cast<int>(blockIdx.x) / num_kv_heads;
+  const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -114,7 +175,7 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   }
   const int t1 = min(n, t0 + partition);
   const int ntok = t1 - t0;
-  const int bs_mask = (1 << log2_bs) - 1;
+  const uint32_t bs_mask = (1u << log2_bs) - 1u;
   const int jb0 = t0 >> log2_bs;
   const int nblk = ((t1 - 1) >> log2_bs) - jb0 + 1;
 
@@ -122,23 +183,27 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   const int32_t* table = block_tables + static_cast<int64_t>(b) * max_blocks;
   for (int i = tid; i < nblk; i += kThreads) s_ids[i] = table[jb0 + i];
 
-  // query slices, pre-scaled so scores land in the log2 domain
-  float qf[G][EPV];
+  QSlice<T> qs[G];
   {
     const char* qrow = q + static_cast<int64_t>(b) * q_stride_bytes;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const Vec16 v = load16(qrow + (static_cast<int64_t>(g * G + h) * D + li * EPV) * EB);
-      E::to_f32(v, qf[h]);
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) qf[h][e] *= scale_log2;
-    }
+    for (int h = 0; h < G; ++h)
+      qs[h].load(load16(qrow + (static_cast<int64_t>(g * G + h) * D + li * EPV) * EB));
   }
   __syncthreads();
 
-  const int64_t row_bytes = static_cast<int64_t>(num_kv_heads) * D * EB;
+  const uint64_t row_bytes = static_cast<uint64_t>(num_kv_heads) * D * EB;
   const int64_t lane_off = static_cast<int64_t>(g) * D * EB + li * 16;
+  const char* kbase = k_cache + lane_off;
+  const char* vbase = v_cache + lane_off;
   const int my_row = wave * TPW + grp;  // row of this lane within a load step
+
+  // byte offset of logical row t0 + tl (rows of the pool fit in 32 bits)
+  auto row_off = [&](int tl) -> uint64_t {
+    const uint32_t pos = static_cast<uint32_t>(t0 + tl);
+    const uint32_t blk = static_cast<uint32_t>(s_ids[(pos >> log2_bs) - jb0]);
+    return static_cast<uint64_t>((blk << log2_bs) + (pos & bs_mask)) * row_bytes;
+  };
 
   // phase 1: scores
   for (int base = 0; base < ntok; base += STEP * kUnroll) {
@@ -146,31 +211,17 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int tl = base + u * STEP + my_row;
-      if (tl < ntok) {
-        const int pos = t0 + tl;
-        const int64_t blk = s_ids[(pos >> log2_bs) - jb0];
-        const int64_t off = ((blk << log2_bs) + (pos & bs_mask)) * row_bytes + lane_off;
-        kv[u] = load16(k_cache + off);
-      } else {
-        kv[u] = Vec16{{0u, 0u, 0u, 0u}};
-      }
+      kv[u] = tl < ntok ? load16(kbase + row_off(tl)) : Vec16{{0u, 0u, 0u, 0u}};
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int tl = base + u * STEP + my_row;
-      float kf[EPV];
-      E::to_f32(kv[u], kf);
       float sc[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) acc = fmaf(qf[h][e], kf[e], acc);
-        sc[h] = group_sum<LPT>(acc);
-      }
+      for (int h = 0; h < G; ++h) sc[h] = group_sum<LPT>(qs[h].dot(kv[u]));
       if (li == 0 && tl < ntok) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) s_score[tl * G + h] = sc[h];
+        for (int h = 0; h < G; ++h) s_score[tl * G + h] = sc[h] * scale_log2;
       }
     }
   }
@@ -207,14 +258,7 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int tl = base + u * STEP + my_row;
-      if (tl < ntok) {
-        const int pos = t0 + tl;
-        const int64_t blk = s_ids[(pos >> log2_bs) - jb0];
-        const int64_t off = ((blk << log2_bs) + (pos & bs_mask)) * row_bytes + lane_off;
-        vv[u] = load16(v_cache + off);
-      } else {
-        vv[u] = Vec16{{0u, 0u, 0u, 0u}};
-      }
+      vv[u] = tl < ntok ? load16(vbase + row_off(tl)) : Vec16{{0u, 0u, 0u, 0u}};
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -280,30 +324,49 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 
 // Log-sum-exp merge of the partition partials of one (sequence, query head):
 //   M = max_p m_p,  L = sum_p l_p 2^(m_p - M),  o = sum_p 2^(m_p - M) acc_p / L.
+// One wave per (sequence, query head): the lanes share the per-partition
+// statistics, then every lane owns D / 64 output elements and sums the
+// partials in partition order (fixed, so the result is reproducible), with
+// the loads of several partitions in flight at once.
 template <typename T, int D>
 __global__ void __launch_bounds__(64) decode_reduce_kernel(
     void* __restrict__ out, const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
     const int32_t* __restrict__ context_lens, int32_t num_q_heads, int32_t partition,
     int32_t num_partitions) {
   constexpr int PER = D / 64;
+  constexpr int kBatch = 8;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int lane = threadIdx.x;
   const int n = context_lens[b];
   const int np = (n + partition - 1) / partition;
   const int64_t slot0 = (static_cast<int64_t>(b) * num_q_heads + h) * num_partitions;
+  const float* ml = ws_ml + slot0 * 2;
+  const float* acc = ws_acc + slot0 * D + lane;
   float o[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) o[k] = 0.f;
   if (np > 0) {
-    float M = -INFINITY;
-    for (int pp = 0; pp < np; ++pp) M = fmaxf(M, ws_ml[(slot0 + pp) * 2]);
-    float L = 0.f;
-    for (int pp = 0; pp < np; ++pp) {
-      const float w = exp2f(ws_ml[(slot0 + pp) * 2] - M);
-      L = fmaf(ws_ml[(slot0 + pp) * 2 + 1], w, L);
+    float m = -INFINITY;
+    for (int pp = lane; pp < np; pp += 64) m = fmaxf(m, ml[2 * pp]);
+    const float M = wave_max(m);
+    float lsum = 0.f;
+    for (int pp = lane; pp < np; pp += 64) lsum += ml[2 * pp + 1] * exp2f(ml[2 * pp] - M);
+    const float L = wave_sum(lsum);
+    for (int p0 = 0; p0 < np; p0 += kBatch) {
+      float w[kBatch];
+      float a[kBatch][PER];
 #pragma unroll
-      for (int k = 0; k < PER; ++k) o[k] = fmaf(w, ws_acc[(slot0 + pp) * D + k * 64 + lane], o[k]);
+      for (int u = 0; u < kBatch; ++u) {
+        const int pp = p0 + u;
+        w[u] = pp < np ? exp2f(ml[2 * pp] - M) : 0.f;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) a[u][k] = pp < np ? acc[static_cast<int64_t>(pp) * D + k * 64] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+        for (int k = 0; k < PER; ++k) o[k] = fmaf(w[u], a[u][k], o[k]);
     }
     const float inv = 1.f / L;
 #pragma unroll
@@ -329,7 +392,7 @@ hipError_t launch_decode_typed(const DecodeArgs& a, hipStream_t stream) {
   const int max_ids = a.partition / (a.block_size < a.partition ? a.block_size : a.partition) + 2;
   const size_t lds = static_cast<size_t>(score_words + 2 * G + max_ids) * 4;
   const float scale_log2 = a.scale * kLog2e;
-  dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
+  dim3 grid(a.num_partitions * a.num_kv_heads, a.num_seqs);
   hipLaunchKernelGGL((decode_partition_kernel<T, D, G>), grid, dim3(kThreads), lds, stream, a.out,
                      static_cast<const char*>(a.q), a.q_stride * EB,
                      static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache),
@@ -358,10 +421,20 @@ hipError_t dispatch_group(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-int32_t decode_partition_tokens(int32_t requested, int32_t block_size, int32_t max_blocks) {
-  (void)block_size;
-  (void)max_blocks;
-  return requested > 0 ? requested : 512;
+int32_t decode_partition_tokens(int32_t requested, int32_t num_seqs, int32_t num_kv_heads,
+                                int32_t group, int32_t block_size, int32_t max_blocks) {
+  if (requested > 0) return requested;
+  // Longest partition (fewest partials to merge) that still gives the grid
+  // enough workgroups to cover the chip several times when every sequence
+  // is as long as its table allows; the LDS score buffer caps group * length.
+  const int64_t max_ctx = static_cast<int64_t>(max_blocks) * block_size;
+  const int64_t want = 8192;
+  for (int32_t part : {1024, 512}) {
+    if (static_cast<int64_t>(group) * part > 8192) continue;
+    const int64_t wgs = static_cast<int64_t>(num_seqs) * num_kv_heads * ((max_ctx + part - 1) / part);
+    if (wgs >= want) return part;
+  }
+  return 256;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

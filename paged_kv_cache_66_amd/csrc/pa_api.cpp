@@ -1,7 +1,7 @@
 // C ABI entry points: argument validation on the host, then one or two
 // kernel launches on the caller's stream. Nothing here reads device memory
 // or synchronises, and no error path enqueues work.
-#include "../../include/pa.h"
+#include "pa.h"
 
 #include <hip/hip_runtime.h>
 
@@ -42,10 +42,12 @@ pa_status check_rows(const void* base, int64_t stride_elems, int64_t row_elems, 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Partition length for a decode call, or -1 when the request is invalid.
-int32_t resolve_partition(int32_t requested, int32_t block_size, int32_t max_blocks) {
+int32_t resolve_partition(int32_t requested, int32_t num_seqs, int32_t num_kv_heads, int32_t group,
+                          int32_t block_size, int32_t max_blocks) {
   if (requested < 0) return -1;
   if (requested > 0 && (requested % 64 != 0 || requested > kMaxPartition)) return -1;
-  return pa::decode_partition_tokens(requested, block_size, max_blocks);
+  return pa::decode_partition_tokens(requested, num_seqs, num_kv_heads, group, block_size,
+                                     max_blocks);
 }
 
 int64_t num_partitions(int32_t partition, int32_t block_size, int32_t max_blocks) {
@@ -94,13 +96,14 @@ pa_status pa_store_kvcache(const void* key, int64_t key_row_stride, const void* 
   return pa::launch_store(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                int32_t block_size, int32_t max_blocks_per_seq,
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                 int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || !is_pow2(block_size) ||
-      max_blocks_per_seq <= 0)
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+      head_dim <= 0 || !is_pow2(block_size) || max_blocks_per_seq <= 0)
     return 0;
-  const int32_t part = resolve_partition(partition_size, block_size, max_blocks_per_seq);
+  const int32_t part = resolve_partition(partition_size, num_seqs, num_kv_heads,
+                                         num_q_heads / num_kv_heads, block_size, max_blocks_per_seq);
   if (part <= 0) return 0;
   const int64_t P = num_partitions(part, block_size, max_blocks_per_seq);
   if (P <= 1) return 0;
@@ -124,7 +127,8 @@ pa_status pa_decode(void* out, const void* q, int64_t q_row_stride, const void* 
   pa_status st = check_head_layout(head_dim, block_size, num_blocks);
   if (st != PA_OK) return st;
   if (!std::isfinite(scale)) return PA_ERR_SHAPE;
-  const int32_t part = resolve_partition(partition_size, block_size, max_blocks_per_seq);
+  const int32_t part = resolve_partition(partition_size, num_seqs, num_kv_heads, G, block_size,
+                                         max_blocks_per_seq);
   if (part <= 0) return PA_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(G) * part > kMaxScoreWords) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
@@ -136,12 +140,12 @@ pa_status pa_decode(void* out, const void* q, int64_t q_row_stride, const void* 
   if ((st = check_rows(q, q_row_stride, static_cast<int64_t>(num_q_heads) * head_dim, eb)) != PA_OK)
     return st;
   const int64_t P = num_partitions(part, block_size, max_blocks_per_seq);
-  if (P > INT32_MAX) return PA_ERR_SHAPE;
+  if (P * num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;  // grid x = partitions * kv heads
   float* ws_acc = nullptr;
   float* ws_ml = nullptr;
   if (P > 1) {
-    const size_t need = pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, block_size,
-                                                 max_blocks_per_seq, partition_size);
+    const size_t need = pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                 block_size, max_blocks_per_seq, partition_size);
     if (workspace == nullptr || workspace_bytes < need) return PA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PA_ERR_ALIGN;
     ws_acc = static_cast<float*>(workspace);

@@ -69,7 +69,9 @@ struct PrefillArgs {
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
-// Partition sizing shared by pa_decode and pa_decode_workspace_size.
-int32_t decode_partition_tokens(int32_t requested, int32_t block_size, int32_t max_blocks);
+// Partition sizing shared by pa_decode and pa_decode_workspace_size
+// (requested > 0 is returned as is; 0 picks the default for the shape).
+int32_t decode_partition_tokens(int32_t requested, int32_t num_seqs, int32_t num_kv_heads,
+                                int32_t group, int32_t block_size, int32_t max_blocks);
 
 }  // namespace pa

@@ -91,16 +91,18 @@ def test_decode_validation(lib):
     assert decode(lib, part=8192) == UNSUP
     assert decode(lib, part=4096, hq=16, hkv=2) == UNSUP  # 8 * 4096 scores exceed LDS
     assert decode(lib, scale=float("inf")) == SHAPE
-    # W * bs = 64 > partition 0 -> default 512: single pass, no workspace needed
-    assert lib.pa_decode_workspace_size(4, 4, 64, 16, 4, 0) == 0
-    # W * bs = 2048 -> 4 partitions of 512: workspace required
-    need = lib.pa_decode_workspace_size(4, 4, 64, 16, 128, 0)
-    assert need == 4 * 4 * 4 * (64 + 2) * 4
+    # W * bs = 64 fits the default partition: single pass, no workspace needed
+    assert lib.pa_decode_workspace_size(4, 4, 2, 64, 16, 4, 0) == 0
+    # W * bs = 2048 with few sequences -> default partition 256: 8 partials
+    need = lib.pa_decode_workspace_size(4, 4, 2, 64, 16, 128, 0)
+    assert need == 4 * 4 * 8 * (64 + 2) * 4
+    # an explicit partition of 512 -> 4 partials
+    assert lib.pa_decode_workspace_size(4, 4, 2, 64, 16, 128, 512) == 4 * 4 * 4 * (64 + 2) * 4
+    assert lib.pa_decode_workspace_size(4, 4, 3, 64, 16, 128, 0) == 0  # invalid group
     assert decode(lib, w=128) == WS
     assert decode(lib, w=128, ws=A, wsn=need - 1) == WS
     assert decode(lib, w=128, ws=A + 4, wsn=need) == ALIGN
-    assert lib.pa_decode_workspace_size(4, 4, 64, 16, 4, 64) == 4 * 4 * 1 * (64 + 2) * 4 or \
-        lib.pa_decode_workspace_size(4, 4, 64, 16, 4, 64) == 0
+    assert lib.pa_decode_workspace_size(4, 4, 2, 64, 16, 4, 64) == 0  # one partition of 64
 
 
 def prefill(lib, **kw):
