@@ -47,7 +47,8 @@
  *   entries of each sequence; context_lens[b] <= max_blocks_per_seq *
  *   block_size; cu_seqlens non-decreasing with 0 <= Lq <= Lk per sequence.
  * Attention is always causal (the pages call both flash-attn kernels with
- *   causal=True), so there is no causal flag. Query head h reads kv head
+ *   causal=True), so there is no causal flag. The softmax scale must be
+ *   finite and > 0 (PA_ERR_SHAPE otherwise). Query head h reads kv head
  *   h / (num_q_heads / num_kv_heads) (contiguous GQA groups).
  */
 #ifndef PA_H_

@@ -211,7 +211,7 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int tl = base + u * STEP + my_row;
-      kv[u] = tl < ntok ? load16(kbase + row_off(tl)) : Vec16{{0u, 0u, 0u, 0u}};
+      kv[u] = tl < ntok ? load16_nt(kbase + row_off(tl)) : Vec16{{0u, 0u, 0u, 0u}};
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -258,7 +258,7 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int tl = base + u * STEP + my_row;
-      vv[u] = tl < ntok ? load16(vbase + row_off(tl)) : Vec16{{0u, 0u, 0u, 0u}};
+      vv[u] = tl < ntok ? load16_nt(vbase + row_off(tl)) : Vec16{{0u, 0u, 0u, 0u}};
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {

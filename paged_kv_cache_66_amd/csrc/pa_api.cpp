@@ -126,7 +126,7 @@ pa_status pa_decode(void* out, const void* q, int64_t q_row_stride, const void* 
   if (num_seqs > kMaxGridYZ || num_kv_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
   pa_status st = check_head_layout(head_dim, block_size, num_blocks);
   if (st != PA_OK) return st;
-  if (!std::isfinite(scale)) return PA_ERR_SHAPE;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return PA_ERR_SHAPE;
   const int32_t part = resolve_partition(partition_size, num_seqs, num_kv_heads, G, block_size,
                                          max_blocks_per_seq);
   if (part <= 0) return PA_ERR_UNSUPPORTED;
@@ -192,7 +192,7 @@ pa_status pa_prefill_varlen(void* out, const void* q, int64_t q_row_stride, int3
   if (num_seqs > kMaxGridYZ || num_kv_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
   pa_status st = check_head_layout(head_dim, block_size, num_blocks);
   if (st != PA_OK) return st;
-  if (!std::isfinite(scale)) return PA_ERR_SHAPE;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return PA_ERR_SHAPE;
   if (block_tables == nullptr) return PA_ERR_UNSUPPORTED;  // packed contiguous mode not built
   if (max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
   if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PA_OK;

@@ -17,6 +17,14 @@ __device__ __forceinline__ Vec16 load16(const void* p) {
   return *reinterpret_cast<const Vec16*>(p);
 }
 
+// Streaming load: the non-temporal hint keeps data that is read once (a
+// sequence's K/V rows in a decode step) from displacing reusable lines.
+__device__ __forceinline__ Vec16 load16_nt(const void* p) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return Vec16{{v.x, v.y, v.z, v.w}};
+}
+
 __device__ __forceinline__ void store16(void* p, const Vec16& v) {
   *reinterpret_cast<Vec16*>(p) = v;
 }

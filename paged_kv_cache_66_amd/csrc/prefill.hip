@@ -22,10 +22,12 @@
 //   the score accumulators (the contraction index is permuted identically on
 //   both operands), and V is written to LDS transposed ([d][key]) so the A
 //   operand is two 8-byte LDS reads;
-// * online softmax in the log2 domain; only the tiles that cross the causal
-//   diagonal or the end of the keys are masked;
-// * the next tile's K/V rows are fetched into registers while the current
-//   tile is being multiplied.
+// * online softmax in the log2 domain: the running max is taken on raw
+//   scores and the scale is folded into the one FMA that feeds exp2; only the
+//   tiles that cross the causal diagonal or the end of the keys are masked;
+// * K/V tiles are double-buffered in LDS: the next tile's rows travel from
+//   HBM into registers while the current tile is multiplied, and one barrier
+//   per tile separates the buffer writes from the reads.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -42,6 +44,13 @@ constexpr int kKeys = 64;   // keys per tile
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const Vec16& v) {
   return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Two fp32 values to packed bf16 (v_cvt_pk_bf16_f32, round to nearest even).
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ uint32_t half16(const Vec16& v, int j) {
@@ -65,8 +74,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   constexpr int KLOADS = kKeys * KCH / kThreads;  // K vectors per thread per tile
   constexpr int VITEMS = (kKeys / 4) * KCH;       // (4-key group, chunk) items per tile
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kKeys * KPITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[D * VPITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKeys * KPITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VPITCH];
 
   const int i = blockIdx.z;
   const int g = blockIdx.y;
@@ -146,13 +155,13 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
       }
     }
   };
-  auto commit = [&]() {
+  auto commit = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < KLOADS; ++u) {
       const int item = tid + u * kThreads;
       const int r = item / KCH;
       const int c = item % KCH;
-      *reinterpret_cast<Vec16*>(&sK[r * KPITCH + c * 8]) = kreg[u];
+      *reinterpret_cast<Vec16*>(&sK[buf][r * KPITCH + c * 8]) = kreg[u];
     }
     if (tid < VITEMS) {
 #pragma unroll
@@ -161,7 +170,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
         uint2 pk;
         pk.x = half16(vreg[0], j) | (half16(vreg[1], j) << 16);
         pk.y = half16(vreg[2], j) | (half16(vreg[3], j) << 16);
-        *reinterpret_cast<uint2*>(&sV[d * VPITCH + vkg * 4]) = pk;
+        *reinterpret_cast<uint2*>(&sV[buf][d * VPITCH + vkg * 4]) = pk;
       }
     }
   };
@@ -174,12 +183,15 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   float m[2] = {-INFINITY, -INFINITY};
   float l[2] = {0.f, 0.f};
 
-  if (nkt > 0) fetch(0);
+  // Tile j is multiplied from LDS buffer j % 2 while tile j + 1 travels from
+  // HBM into registers; it is written to the other buffer afterwards, and a
+  // single barrier per tile separates the writes from the next reads.
+  fetch(0);
+  commit(0);
+  __syncthreads();
   for (int j = 0; j < nkt; ++j) {
     const int kt0 = j * kKeys;
-    __syncthreads();  // previous tile fully consumed
-    commit();
-    __syncthreads();
+    const int buf = j & 1;
     if (j + 1 < nkt) fetch(kt0 + kKeys);
 
     // S^T tile: 64 keys x 32 (head, query) columns per wave
@@ -192,7 +204,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const Vec16 kv = *reinterpret_cast<const Vec16*>(&sK[(kt * 16 + col) * KPITCH + ks * 32 + gq * 8]);
+        const Vec16 kv = *reinterpret_cast<const Vec16*>(&sK[buf][(kt * 16 + col) * KPITCH + ks * 32 + gq * 8]);
         const bf16x8_t ka = as_bf16x8(kv);
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -204,22 +216,21 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
     uint32_t pop[2][2][4];  // [k-step of 32 keys][t][packed pair]
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      // raw-score max (scale > 0 keeps the order); masked keys are -inf
       float tmax = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float v = s[kt][t][e] * scale_log2;
           if (need_mask) {
             const int key = kt0 + kt * 16 + gq * 4 + e;
-            if (key > posq[t] || key >= Lk) v = -INFINITY;
+            if (key > posq[t] || key >= Lk) s[kt][t][e] = -INFINITY;
           }
-          s[kt][t][e] = v;
-          tmax = fmaxf(tmax, v);
+          tmax = fmaxf(tmax, s[kt][t][e]);
         }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m[t], tmax);
+      const float m_new = fmaxf(m[t], tmax * scale_log2);
       const float alpha = exp2f(m[t] - m_new);
       m[t] = m_new;
       float lsum = 0.f;
@@ -227,7 +238,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p = exp2f(s[kt][t][e] - m_new);
+          const float p = exp2f(fmaf(s[kt][t][e], scale_log2, -m_new));
           s[kt][t][e] = p;
           lsum += p;
         }
@@ -236,10 +247,10 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
       for (int dt = 0; dt < DT; ++dt) o[dt][t] *= alpha;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        pop[st][t][0] = pack_bf16x2(s[2 * st][t][0], s[2 * st][t][1]);
-        pop[st][t][1] = pack_bf16x2(s[2 * st][t][2], s[2 * st][t][3]);
-        pop[st][t][2] = pack_bf16x2(s[2 * st + 1][t][0], s[2 * st + 1][t][1]);
-        pop[st][t][3] = pack_bf16x2(s[2 * st + 1][t][2], s[2 * st + 1][t][3]);
+        pop[st][t][0] = pack2(s[2 * st][t][0], s[2 * st][t][1]);
+        pop[st][t][1] = pack2(s[2 * st][t][2], s[2 * st][t][3]);
+        pop[st][t][2] = pack2(s[2 * st + 1][t][0], s[2 * st + 1][t][1]);
+        pop[st][t][3] = pack2(s[2 * st + 1][t][2], s[2 * st + 1][t][3]);
       }
     }
 
@@ -248,7 +259,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const uint16_t* vrow = &sV[(dt * 16 + col) * VPITCH + st * 32 + gq * 4];
+        const uint16_t* vrow = &sV[buf][(dt * 16 + col) * VPITCH + st * 32 + gq * 4];
         const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
         const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
         const Vec16 va{{lo.x, lo.y, hi.x, hi.y}};
@@ -260,6 +271,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
         }
       }
     }
+    if (j + 1 < nkt) commit(buf ^ 1);
+    __syncthreads();
   }
 
   // ---- normalise and write ----
@@ -274,8 +287,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       uint2 w;
-      w.x = pack_bf16x2(o[dt][t][0] * inv, o[dt][t][1] * inv);
-      w.y = pack_bf16x2(o[dt][t][2] * inv, o[dt][t][3] * inv);
+      w.x = pack2(o[dt][t][0] * inv, o[dt][t][1] * inv);
+      w.y = pack2(o[dt][t][2] * inv, o[dt][t][3] * inv);
       *reinterpret_cast<uint2*>(orow_ptr + dt * 16 + gq * 4) = w;
     }
   }

@@ -91,6 +91,8 @@ def test_decode_validation(lib):
     assert decode(lib, part=8192) == UNSUP
     assert decode(lib, part=4096, hq=16, hkv=2) == UNSUP  # 8 * 4096 scores exceed LDS
     assert decode(lib, scale=float("inf")) == SHAPE
+    assert decode(lib, scale=0.0) == SHAPE
+    assert decode(lib, scale=-0.5) == SHAPE
     # W * bs = 64 fits the default partition: single pass, no workspace needed
     assert lib.pa_decode_workspace_size(4, 4, 2, 64, 16, 4, 0) == 0
     # W * bs = 2048 with few sequences -> default partition 256: 8 partials
@@ -125,6 +127,8 @@ def test_prefill_validation(lib):
     assert prefill(lib, qs=256) == SHAPE
     assert prefill(lib, out=A + 2) == ALIGN
     assert prefill(lib, mq=-1) == SHAPE
+    assert prefill(lib, scale=0.0) == SHAPE
+    assert prefill(lib, scale=float("nan")) == SHAPE
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
