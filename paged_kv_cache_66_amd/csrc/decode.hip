@@ -61,10 +61,10 @@ __device__ __forceinline__ float dpp_add(float v) {
 // only a 32-lane group needs a cross-row exchange.
 template <int LPT>
 __device__ __forceinline__ float group_sum(float v) {
-  static_assert(LPT == 8 || LPT == 16 || LPT == 32, "lanes per row");
+  static_assert(LPT == 4 || LPT == 8 || LPT == 16 || LPT == 32, "lanes per row");
   v = dpp_add<kDppQuadXor1>(v);
   v = dpp_add<kDppQuadXor2>(v);
-  v = dpp_add<kDppRowHalfMirror>(v);
+  if constexpr (LPT >= 8) v = dpp_add<kDppRowHalfMirror>(v);
   if constexpr (LPT >= 16) v = dpp_add<kDppRowMirror>(v);
   if constexpr (LPT == 32) v += __shfl_xor(v, 16, 64);
   return v;
@@ -82,39 +82,52 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Query slice of one head held by a lane, in the form the score dot product
-// wants: fp32 values for fp32 caches, raw bf16 pairs for bf16 caches (the
-// products of two bf16 values are exact in fp32, so v_dot2_f32_bf16 computes
-// the same partial sums as widening first, with no conversion instructions).
+// Query slice of one head held by a lane for the score pass: two 16-byte
+// vectors of the head's row, in the form the dot product wants: fp32 values
+// for fp32 caches, raw bf16 pairs for bf16 caches (products of two bf16
+// values are exact in fp32, so v_dot2_f32_bf16 computes the same partial sums
+// as widening first, with no conversion instructions).
 template <typename T> struct QSlice;
 
 template <> struct QSlice<float> {
-  float v[4];
-  __device__ __forceinline__ void load(const Vec16& x) {
+  float v[8];
+  __device__ __forceinline__ void load(const Vec16& x0, const Vec16& x1) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(x.w[e]);
+    for (int e = 0; e < 4; ++e) {
+      v[e] = __uint_as_float(x0.w[e]);
+      v[4 + e] = __uint_as_float(x1.w[e]);
+    }
   }
-  __device__ __forceinline__ float dot(const Vec16& k) const {
+  __device__ __forceinline__ float dot(const Vec16& k0, const Vec16& k1) const {
     float acc = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc = fmaf(v[e], __uint_as_float(k.w[e]), acc);
+    for (int e = 0; e < 4; ++e) acc = fmaf(v[e], __uint_as_float(k0.w[e]), acc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fmaf(v[4 + e], __uint_as_float(k1.w[e]), acc);
     return acc;
   }
 };
 
 template <> struct QSlice<BF16Tag> {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  uint32_t v[4];
-  __device__ __forceinline__ void load(const Vec16& x) {
+  uint32_t v[8];
+  __device__ __forceinline__ void load(const Vec16& x0, const Vec16& x1) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) v[w] = x.w[w];
+    for (int w = 0; w < 4; ++w) {
+      v[w] = x0.w[w];
+      v[4 + w] = x1.w[w];
+    }
   }
-  __device__ __forceinline__ float dot(const Vec16& k) const {
+  __device__ __forceinline__ float dot(const Vec16& k0, const Vec16& k1) const {
     float acc = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
       acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v[w]),
-                                            __builtin_bit_cast(bf16x2_t, k.w[w]), acc, false);
+                                            __builtin_bit_cast(bf16x2_t, k0.w[w]), acc, false);
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v[4 + w]),
+                                            __builtin_bit_cast(bf16x2_t, k1.w[w]), acc, false);
     return acc;
   }
 };
@@ -133,6 +146,12 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   using E = Elem<T>;
   constexpr int EPV = E::kPerVec;    // elements per 16-byte vector
   constexpr int EB = E::kBytes;      // bytes per element
+  // score pass: a (token, kv head) row is spread over LPT1 lanes holding two
+  // 16-byte vectors each (fewer lanes per row -> fewer reduction steps)
+  constexpr int LPT1 = D / (2 * EPV);
+  constexpr int TPW1 = 64 / LPT1;
+  constexpr int STEP1 = kWaves * TPW1;
+  // value pass: LPT lanes per row, one vector each (fewer accumulators)
   constexpr int LPT = D / EPV;       // lanes per (token, kv head) row
   constexpr int TPW = 64 / LPT;      // rows per wave per load
   constexpr int STEP = kWaves * TPW; // rows per workgroup per load
@@ -143,11 +162,13 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   float* s_sum = s_max + G;                               // [G]
   int32_t* s_ids = reinterpret_cast<int32_t*>(s_sum + G);  // block ids of the partition
 
-  // The kv heads of one partition are adjacent in dispatch order, so the
-  // workgroups reading the slices of the same token rows run together.
+  // Dispatch order: kv head fastest, then sequence, then partition. The
+  // workgroups that read the head slices of the same token rows run side by
+  // side, and sequences that share prefix blocks read them at the same time.
+  const int num_seqs = gridDim.x / (num_kv_heads * num_partitions);
   const int g = static_cast<int>(blockIdx.x) % num_kv_heads;
-  const int p = static_cast<int>(blockIdx.x) / num_kv_heads;
-  const int b = blockIdx.y;
+  const int b = (static_cast<int>(blockIdx.x) / num_kv_heads) % num_seqs;
+  const int p = static_cast<int>(blockIdx.x) / (num_kv_heads * num_seqs);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -183,18 +204,21 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   const int32_t* table = block_tables + static_cast<int64_t>(b) * max_blocks;
   for (int i = tid; i < nblk; i += kThreads) s_ids[i] = table[jb0 + i];
 
+  const int grp1 = lane / LPT1;
+  const int li1 = lane % LPT1;
   QSlice<T> qs[G];
   {
     const char* qrow = q + static_cast<int64_t>(b) * q_stride_bytes;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-      qs[h].load(load16(qrow + (static_cast<int64_t>(g * G + h) * D + li * EPV) * EB));
+    for (int h = 0; h < G; ++h) {
+      const char* qh = qrow + static_cast<int64_t>(g * G + h) * D * EB;
+      qs[h].load(load16(qh + li1 * 16), load16(qh + (LPT1 + li1) * 16));
+    }
   }
   __syncthreads();
 
   const uint64_t row_bytes = static_cast<uint64_t>(num_kv_heads) * D * EB;
   const int64_t lane_off = static_cast<int64_t>(g) * D * EB + li * 16;
-  const char* kbase = k_cache + lane_off;
   const char* vbase = v_cache + lane_off;
   const int my_row = wave * TPW + grp;  // row of this lane within a load step
 
@@ -205,36 +229,47 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
     return static_cast<uint64_t>((blk << log2_bs) + (pos & bs_mask)) * row_bytes;
   };
 
-  // phase 1: scores
-  for (int base = 0; base < ntok; base += STEP * kUnroll) {
-    Vec16 kv[kUnroll];
+  // phase 1: raw scores q . k (the scale is applied once per score in phase 2)
+  const char* kbase1 = k_cache + static_cast<int64_t>(g) * D * EB + li1 * 16;
+  const int my_row1 = wave * TPW1 + grp1;
+  for (int base = 0; base < ntok; base += STEP1 * kUnroll) {
+    Vec16 k0[kUnroll], k1[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int tl = base + u * STEP + my_row;
-      kv[u] = tl < ntok ? load16_nt(kbase + row_off(tl)) : Vec16{{0u, 0u, 0u, 0u}};
+      const int tl = base + u * STEP1 + my_row1;
+      if (tl < ntok) {
+        const char* r = kbase1 + row_off(tl);
+        k0[u] = load16_nt(r);
+        k1[u] = load16_nt(r + LPT1 * 16);
+      } else {
+        k0[u] = Vec16{{0u, 0u, 0u, 0u}};
+        k1[u] = k0[u];
+      }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int tl = base + u * STEP + my_row;
+      const int tl = base + u * STEP1 + my_row1;
       float sc[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) sc[h] = group_sum<LPT>(qs[h].dot(kv[u]));
-      if (li == 0 && tl < ntok) {
+      for (int h = 0; h < G; ++h) sc[h] = group_sum<LPT1>(qs[h].dot(k0[u], k1[u]));
+      if (li1 == 0 && tl < ntok) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) s_score[tl * G + h] = sc[h] * scale_log2;
+        for (int h = 0; h < G; ++h) s_score[tl * G + h] = sc[h];
       }
     }
   }
   __syncthreads();
 
-  // phase 2: exact max and sum of exp2(s - max) per head; p overwrites s
+  // phase 2: exact max and sum of exp2(s - max) per head, in the log2 domain
+  // (s = raw score * scale * log2 e; scale > 0 so the raw max is the max);
+  // p overwrites the raw score
   for (int h = wave; h < G; h += kWaves) {
     float m = -INFINITY;
     for (int t = lane; t < ntok; t += 64) m = fmaxf(m, s_score[t * G + h]);
-    m = wave_max(m);
+    m = wave_max(m) * scale_log2;
     float l = 0.f;
     for (int t = lane; t < ntok; t += 64) {
-      const float e = exp2f(s_score[t * G + h] - m);
+      const float e = exp2f(fmaf(s_score[t * G + h], scale_log2, -m));
       s_score[t * G + h] = e;
       l += e;
     }
@@ -392,7 +427,7 @@ hipError_t launch_decode_typed(const DecodeArgs& a, hipStream_t stream) {
   const int max_ids = a.partition / (a.block_size < a.partition ? a.block_size : a.partition) + 2;
   const size_t lds = static_cast<size_t>(score_words + 2 * G + max_ids) * 4;
   const float scale_log2 = a.scale * kLog2e;
-  dim3 grid(a.num_partitions * a.num_kv_heads, a.num_seqs);
+  dim3 grid(a.num_partitions * a.num_kv_heads * a.num_seqs);
   hipLaunchKernelGGL((decode_partition_kernel<T, D, G>), grid, dim3(kThreads), lds, stream, a.out,
                      static_cast<const char*>(a.q), a.q_stride * EB,
                      static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache),

@@ -140,7 +140,8 @@ pa_status pa_decode(void* out, const void* q, int64_t q_row_stride, const void* 
   if ((st = check_rows(q, q_row_stride, static_cast<int64_t>(num_q_heads) * head_dim, eb)) != PA_OK)
     return st;
   const int64_t P = num_partitions(part, block_size, max_blocks_per_seq);
-  if (P * num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;  // grid x = partitions * kv heads
+  // grid x = partitions * kv heads * sequences
+  if (P * num_kv_heads * num_seqs > INT32_MAX) return PA_ERR_SHAPE;
   float* ws_acc = nullptr;
   float* ws_ml = nullptr;
   if (P > 1) {

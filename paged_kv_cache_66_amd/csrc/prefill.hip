@@ -41,10 +41,16 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kRows = 128;  // (head, query) rows per workgroup
 constexpr int kKeys = 64;   // keys per tile
+constexpr int kXcds = 8;    // accelerator complex dies of an MI355X
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const Vec16& v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
+
+// 2^x on the hardware exp unit (v_exp_f32). Arguments here are <= 0;
+// results below the normal range flush to zero, which softmax weights
+// tolerate (they are summed against weights of order one).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Two fp32 values to packed bf16 (v_cvt_pk_bf16_f32, round to nearest even).
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
@@ -64,7 +70,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
     const char* __restrict__ k_cache, const char* __restrict__ v_cache,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
     const int32_t* __restrict__ block_tables, int32_t max_blocks, int32_t num_q_heads,
-    int32_t num_kv_heads, int32_t log2_bs, float scale_log2) {
+    int32_t num_kv_heads, int32_t log2_bs, float scale_log2, int32_t max_qt) {
   constexpr int QT = kRows / G;    // queries per workgroup
   constexpr int KS = D / 32;       // MFMA k-steps over head_dim
   constexpr int DT = D / 16;       // 16-wide head_dim tiles of the output
@@ -77,14 +83,34 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKeys * KPITCH];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VPITCH];
 
-  const int i = blockIdx.z;
-  const int g = blockIdx.y;
+  // Workgroups are handed to the 8 XCDs round-robin by linear id, and each
+  // XCD has its own L2. Route every kv head to one XCD (g % 8 == id % 8) and
+  // put the query tiles of a (sequence, kv head) next to each other, so the
+  // tiles that stream the same K/V rows share an L2.
+  int i, g, x;
+  {
+    const int L = blockIdx.x;
+    if (num_kv_heads % kXcds == 0) {
+      const int xcd = L % kXcds;
+      const int r = L / kXcds;
+      const int heads_per_xcd = num_kv_heads / kXcds;
+      x = r % max_qt;
+      const int r2 = r / max_qt;
+      g = (r2 % heads_per_xcd) * kXcds + xcd;
+      i = r2 / heads_per_xcd;
+    } else {
+      x = L % max_qt;
+      const int r = L / max_qt;
+      g = r % num_kv_heads;
+      i = r / num_kv_heads;
+    }
+  }
   const int q0 = cu_q[i];
   const int Lq = cu_q[i + 1] - q0;
   const int Lk = cu_k[i + 1] - cu_k[i];
   const int n_qt = (Lq + QT - 1) / QT;
-  if (static_cast<int>(blockIdx.x) >= n_qt) return;
-  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x);  // heaviest tiles first
+  if (x >= n_qt) return;
+  const int qt = n_qt - 1 - x;  // heaviest tiles first
   const int q_lo = qt * QT;
   const int q_hi = min(q_lo + QT, Lq);
   const int start = Lk - Lq;
@@ -128,6 +154,10 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   const int32_t* table = block_tables + static_cast<int64_t>(i) * max_blocks;
   const int bs_mask = (1 << log2_bs) - 1;
 
+  // Byte offset of key row `key` of this sequence (kv head slice included).
+  // With blocks of at least one tile (64 keys) a tile lies inside one block,
+  // so its block id is read once per tile; smaller blocks look up every row.
+  const bool tile_in_block = log2_bs >= 6;
   auto row_addr = [&](int key) -> int64_t {
     const int64_t blk = table[key >> log2_bs];
     return ((blk << log2_bs) + (key & bs_mask)) * row_bytes + head_off;
@@ -139,19 +169,23 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   const int vkg = tid % (kKeys / 4);  // 4-key group of the V item
   const int vdc = tid / (kKeys / 4);  // 16-byte chunk of the V item
   auto fetch = [&](int kt0) {
+    const int64_t tile_base = tile_in_block ? row_addr(kt0) : 0;  // kt0 < Lk always
 #pragma unroll
     for (int u = 0; u < KLOADS; ++u) {
       const int item = tid + u * kThreads;
       const int r = item / KCH;
       const int c = item % KCH;
       const int key = kt0 + r;
-      kreg[u] = key < Lk ? load16(k_cache + row_addr(key) + c * 16) : Vec16{{0u, 0u, 0u, 0u}};
+      const int64_t off = tile_in_block ? tile_base + r * row_bytes : row_addr(key);
+      kreg[u] = key < Lk ? load16(k_cache + off + c * 16) : Vec16{{0u, 0u, 0u, 0u}};
     }
     if (tid < VITEMS) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int key = kt0 + vkg * 4 + e;
-        vreg[e] = key < Lk ? load16(v_cache + row_addr(key) + vdc * 16) : Vec16{{0u, 0u, 0u, 0u}};
+        const int r = vkg * 4 + e;
+        const int key = kt0 + r;
+        const int64_t off = tile_in_block ? tile_base + r * row_bytes : row_addr(key);
+        vreg[e] = key < Lk ? load16(v_cache + off + vdc * 16) : Vec16{{0u, 0u, 0u, 0u}};
       }
     }
   };
@@ -216,35 +250,43 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
     uint32_t pop[2][2][4];  // [k-step of 32 keys][t][packed pair]
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      if (need_mask) {
+        // key kt0 + kt*16 + gq*4 + e is visible to this column iff it is at
+        // most lim (the query's position, capped by the last key)
+        const int lim = min(posq[t], Lk - 1) - (kt0 + gq * 4);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            s[kt][t][e] = (kt * 16 + e <= lim) ? s[kt][t][e] : -INFINITY;
+      }
       // raw-score max (scale > 0 keeps the order); masked keys are -inf
       float tmax = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (need_mask) {
-            const int key = kt0 + kt * 16 + gq * 4 + e;
-            if (key > posq[t] || key >= Lk) s[kt][t][e] = -INFINITY;
-          }
-          tmax = fmaxf(tmax, s[kt][t][e]);
-        }
+        tmax = fmaxf(tmax, fmaxf(fmaxf(s[kt][t][0], s[kt][t][1]), fmaxf(s[kt][t][2], s[kt][t][3])));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
       const float m_new = fmaxf(m[t], tmax * scale_log2);
-      const float alpha = exp2f(m[t] - m_new);
+      // The O rows are rescaled only when some column's max moved; once the
+      // first tiles have been seen that is rare.
+      if (__any(m_new != m[t])) {
+        const float alpha = fast_exp2(m[t] - m_new);
+        l[t] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt][t] *= alpha;
+      }
       m[t] = m_new;
       float lsum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p = exp2f(fmaf(s[kt][t][e], scale_log2, -m_new));
+          const float p = fast_exp2(fmaf(s[kt][t][e], scale_log2, -m_new));
           s[kt][t][e] = p;
           lsum += p;
         }
-      l[t] = l[t] * alpha + lsum;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt][t] *= alpha;
+      l[t] += lsum;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         pop[st][t][0] = pack2(s[2 * st][t][0], s[2 * st][t][1]);
@@ -301,12 +343,14 @@ hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
   while ((1 << log2_bs) < a.block_size) ++log2_bs;
   const int max_qt = (a.max_seqlen_q + QT - 1) / QT;
   if (max_qt == 0 || a.num_seqs == 0) return hipSuccess;
-  dim3 grid(max_qt, a.num_kv_heads, a.num_seqs);
+  const int64_t total = static_cast<int64_t>(max_qt) * a.num_kv_heads * a.num_seqs;
+  if (total > INT32_MAX) return hipErrorInvalidValue;
+  dim3 grid(static_cast<uint32_t>(total));
   hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(kThreads), 0, stream,
                      static_cast<uint16_t*>(a.out), static_cast<const char*>(a.q), a.q_stride * 2,
                      static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache), a.cu_q,
                      a.cu_k, a.block_tables, a.max_blocks, a.num_q_heads, a.num_kv_heads, log2_bs,
-                     a.scale * kLog2e);
+                     a.scale * kLog2e, max_qt);
   return hipGetLastError();
 }
 

@@ -1,0 +1,74 @@
+"""Run one hot-path operation a few times, for rocprofv3.
+
+    rocprofv3 --kernel-trace --stats --output-format csv -d OUT -o run -- \\
+        python3 -m paged_kv_cache_66_amd.profile_ops decode qwen3-0.6b-decode
+
+Operations:
+  decode <workload>   pa_store_kvcache of the new tokens + pa_decode, inputs
+                      resident, a 1 GiB read between calls (cold caches);
+  prefill             pa_store_kvcache + pa_prefill_varlen on chunked-prefill;
+  copy                a 1 GiB device-to-device copy (counter calibration:
+                      reads 1 GiB, writes 1 GiB).
+Workloads are the seeded synthetic ones of ``workloads.py``.
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("op", choices=["decode", "prefill", "copy"])
+    ap.add_argument("workload", nargs="?", default="qwen3-0.6b-decode")
+    ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--partition", type=int, default=0)
+    args = ap.parse_args(argv)
+
+    import torch
+
+    from paged_kv_cache_66_amd import binding
+    from paged_kv_cache_66_amd import workloads as wl
+
+    binding.load()
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    if args.op == "copy":
+        dst = torch.empty_like(scratch)
+        for _ in range(args.reps):
+            dst.copy_(scratch)
+    elif args.op == "prefill":
+        w = wl.chunked_prefill(0)
+        t = wl.make_device_tensors(w)
+        slots = torch.from_numpy(w.slot_mapping).cuda()
+        cuq = torch.from_numpy(w.cu_seqlens_q).cuda()
+        cuk = torch.from_numpy(w.cu_seqlens_k).cuda()
+        tables = torch.from_numpy(w.block_tables).cuda()
+        out = torch.empty((w.total_q, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+        for _ in range(args.reps):
+            scratch.amax()
+            binding.pa_store_kvcache(t["k"], t["v"], t["k_cache"], t["v_cache"], slots)
+            binding.pa_prefill_varlen(t["q"], t["k_cache"], t["v_cache"], cuq, cuk, w.max_seqlen_q,
+                                      w.max_seqlen_k, tables, w.scale, out=out)
+    else:
+        w = wl.DECODE_CONFIGS[args.workload](0)
+        t = wl.make_device_tensors(w)
+        slots = torch.from_numpy(w.slot_mapping).cuda()
+        tables = torch.from_numpy(w.block_tables).cuda()
+        ctx = torch.from_numpy(w.context_lens).cuda()
+        out = torch.empty_like(t["q"].contiguous())
+        for _ in range(args.reps):
+            scratch.amax()
+            binding.pa_store_kvcache(t["k"], t["v"], t["k_cache"], t["v_cache"], slots)
+            binding.pa_decode(t["q"], t["k_cache"], t["v_cache"], tables, ctx, w.scale, out=out,
+                              partition_size=args.partition)
+    torch.cuda.synchronize()
+    print(f"profile_ops {args.op} {args.workload if args.op == 'decode' else ''} done", flush=True)
+
+
+if __name__ == "__main__":
+    main()
