@@ -38,8 +38,9 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kRows = 128;  // (head, query) rows per workgroup
+constexpr int kWavesPerGroup = 4;
+constexpr int kThreads = 64 * kWavesPerGroup;
+constexpr int kRows = 32 * kWavesPerGroup;  // (head, query) rows per workgroup: 32 per wave
 constexpr int kKeys = 64;   // keys per tile
 constexpr int kXcds = 8;    // accelerator complex dies of an MI355X
 
@@ -78,7 +79,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   constexpr int VPITCH = kKeys + 4;  // bf16 per transposed V row in LDS
   constexpr int KCH = D / 8;       // 16-byte chunks per K row
   constexpr int KLOADS = kKeys * KCH / kThreads;  // K vectors per thread per tile
-  constexpr int VITEMS = (kKeys / 4) * KCH;       // (4-key group, chunk) items per tile
+  constexpr int VK = kKeys * KCH / kThreads;      // V rows per thread per tile (same chunk)
+  constexpr int VGROUPS = kKeys / VK;             // V row groups per tile
+  static_assert(VK == 1 || VK == 2 || VK == 4, "V rows per thread");
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKeys * KPITCH];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VPITCH];
@@ -165,9 +168,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
 
   // ---- tile fetch into registers ----
   Vec16 kreg[KLOADS];
-  Vec16 vreg[4];
-  const int vkg = tid % (kKeys / 4);  // 4-key group of the V item
-  const int vdc = tid / (kKeys / 4);  // 16-byte chunk of the V item
+  Vec16 vreg[VK];
+  const int vkg = tid % VGROUPS;  // group of VK consecutive V rows of the item
+  const int vdc = tid / VGROUPS;  // 16-byte chunk of the V item
   auto fetch = [&](int kt0) {
     const int64_t tile_base = tile_in_block ? row_addr(kt0) : 0;  // kt0 < Lk always
 #pragma unroll
@@ -179,14 +182,12 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
       const int64_t off = tile_in_block ? tile_base + r * row_bytes : row_addr(key);
       kreg[u] = key < Lk ? load16(k_cache + off + c * 16) : Vec16{{0u, 0u, 0u, 0u}};
     }
-    if (tid < VITEMS) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = vkg * 4 + e;
-        const int key = kt0 + r;
-        const int64_t off = tile_in_block ? tile_base + r * row_bytes : row_addr(key);
-        vreg[e] = key < Lk ? load16(v_cache + off + vdc * 16) : Vec16{{0u, 0u, 0u, 0u}};
-      }
+    for (int e = 0; e < VK; ++e) {
+      const int r = vkg * VK + e;
+      const int key = kt0 + r;
+      const int64_t off = tile_in_block ? tile_base + r * row_bytes : row_addr(key);
+      vreg[e] = key < Lk ? load16(v_cache + off + vdc * 16) : Vec16{{0u, 0u, 0u, 0u}};
     }
   };
   auto commit = [&](int buf) {
@@ -197,14 +198,20 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
       const int c = item % KCH;
       *reinterpret_cast<Vec16*>(&sK[buf][r * KPITCH + c * 8]) = kreg[u];
     }
-    if (tid < VITEMS) {
+    // V goes to LDS transposed: element j of the chunk is row vdc * 8 + j of
+    // sV, and the VK keys of this item sit side by side in that row
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int d = vdc * 8 + j;
+    for (int j = 0; j < 8; ++j) {
+      uint16_t* dst = &sV[buf][(vdc * 8 + j) * VPITCH + vkg * VK];
+      if constexpr (VK == 4) {
         uint2 pk;
         pk.x = half16(vreg[0], j) | (half16(vreg[1], j) << 16);
         pk.y = half16(vreg[2], j) | (half16(vreg[3], j) << 16);
-        *reinterpret_cast<uint2*>(&sV[buf][d * VPITCH + vkg * 4]) = pk;
+        *reinterpret_cast<uint2*>(dst) = pk;
+      } else if constexpr (VK == 2) {
+        *reinterpret_cast<uint32_t*>(dst) = half16(vreg[0], j) | (half16(vreg[1], j) << 16);
+      } else {
+        *dst = static_cast<uint16_t>(half16(vreg[0], j));
       }
     }
   };

@@ -2,15 +2,23 @@
 
     python3 -m paged_kv_cache_66_amd.profile_summary stats OUT/run_kernel_stats.csv
     python3 -m paged_kv_cache_66_amd.profile_summary pmc OUT/run_counter_collection.csv
+    python3 -m paged_kv_cache_66_amd.profile_summary traffic KFETCH KWRITE CFETCH CWRITE \
+        COPY_BYTES SOURCE NAME...
 
 `stats` lists per-kernel call counts and durations; `pmc` averages every
-collected counter per kernel over its dispatches. Kernel names are shortened
-to the function name with template arguments.
+collected counter per kernel over its dispatches. `traffic` turns FETCH_SIZE
+and WRITE_SIZE runs (KiB per dispatch) of the kernels whose names contain one
+of NAME... into HBM bytes per launch of the whole call, each counter scaled
+by the ratio of known bytes to what the same counter read for a plain copy
+of COPY_BYTES bytes, and stamps the result with the SHA-256 of SOURCE (the
+figure is stale once that file changes). Kernel names are shortened to the
+function name with template arguments.
 """
 from __future__ import annotations
 
 import collections
 import csv
+import os
 import sys
 
 
@@ -45,9 +53,47 @@ def pmc(path: str, only: str = "") -> str:
     return "\n".join(out)
 
 
+def _per_dispatch(path: str, counter: str, names) -> dict:
+    """Mean counter value per kernel (shortened name) over its dispatches."""
+    acc = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        if names and not any(n in r["Kernel_Name"] for n in names):
+            continue
+        acc[short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def traffic(kfetch, kwrite, cfetch, cwrite, copy_bytes, source, names) -> dict:
+    import hashlib
+    import json  # noqa: F401
+
+    cf = _per_dispatch(cfetch, "FETCH_SIZE", ["copy"])
+    cw = _per_dispatch(cwrite, "WRITE_SIZE", ["copy"])
+    fetch_factor = copy_bytes / (max(cf.values()) * 1024)
+    write_factor = copy_bytes / (max(cw.values()) * 1024)
+    kf = _per_dispatch(kfetch, "FETCH_SIZE", names)
+    kw = _per_dispatch(kwrite, "WRITE_SIZE", names)
+    per_kernel = {k: {"fetch_bytes": kf.get(k, 0) * 1024 * fetch_factor,
+                      "write_bytes": kw.get(k, 0) * 1024 * write_factor} for k in sorted(set(kf) | set(kw))}
+    total = sum(v["fetch_bytes"] + v["write_bytes"] for v in per_kernel.values())
+    with open(source, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    return {"bytes_per_launch": round(total), "fetch_factor": round(fetch_factor, 4),
+            "write_factor": round(write_factor, 4), "per_kernel": per_kernel,
+            "kernel_sha256": sha, "source": os.path.basename(source)}
+
+
 def main(argv=None):
     argv = sys.argv[1:] if argv is None else argv
-    kind, path = argv[0], argv[1]
+    kind = argv[0]
+    if kind == "traffic":
+        import json
+        rec = traffic(argv[1], argv[2], argv[3], argv[4], float(argv[5]), argv[6], argv[7:])
+        print(json.dumps(rec, indent=1))
+        return
+    path = argv[1]
     only = argv[2] if len(argv) > 2 else ""
     print(stats(path, only) if kind == "stats" else pmc(path, only))
 
