@@ -60,6 +60,15 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // (1.0, 1.0) in bf16
+
+// a.x * b.x + a.y * b.y + c for packed bf16 pairs, fp32 accumulate
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b),
+                                         c, false);
+}
+
 __device__ __forceinline__ uint32_t half16(const Vec16& v, int j) {
   const uint32_t w = v.w[j >> 1];
   return (j & 1) ? (w >> 16) : (w & 0xffffu);
@@ -171,23 +180,45 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   Vec16 vreg[VK];
   const int vkg = tid % VGROUPS;  // group of VK consecutive V rows of the item
   const int vdc = tid / VGROUPS;  // 16-byte chunk of the V item
+  // Byte offsets of this thread's K and V vectors inside a tile that lies in
+  // one block (rows x row size + chunk: under 2^31 for any supported shape);
+  // fixed for the whole kernel, so a tile fetch adds one uniform base.
+  uint32_t koff[KLOADS];
+  uint32_t voff[VK];
+#pragma unroll
+  for (int u = 0; u < KLOADS; ++u) {
+    const int item = tid + u * kThreads;
+    koff[u] = static_cast<uint32_t>((item / KCH) * row_bytes + (item % KCH) * 16);
+  }
+#pragma unroll
+  for (int e = 0; e < VK; ++e) voff[e] = static_cast<uint32_t>((vkg * VK + e) * row_bytes + vdc * 16);
+
   auto fetch = [&](int kt0) {
-    const int64_t tile_base = tile_in_block ? row_addr(kt0) : 0;  // kt0 < Lk always
+    if (tile_in_block) {
+      const char* kb = k_cache + row_addr(kt0);  // kt0 < Lk always
+      const char* vb = v_cache + row_addr(kt0);
+#pragma unroll
+      for (int u = 0; u < KLOADS; ++u) {
+        const int key = kt0 + (tid + u * kThreads) / KCH;
+        kreg[u] = key < Lk ? load16(kb + koff[u]) : Vec16{{0u, 0u, 0u, 0u}};
+      }
+#pragma unroll
+      for (int e = 0; e < VK; ++e) {
+        const int key = kt0 + vkg * VK + e;
+        vreg[e] = key < Lk ? load16(vb + voff[e]) : Vec16{{0u, 0u, 0u, 0u}};
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < KLOADS; ++u) {
       const int item = tid + u * kThreads;
-      const int r = item / KCH;
-      const int c = item % KCH;
-      const int key = kt0 + r;
-      const int64_t off = tile_in_block ? tile_base + r * row_bytes : row_addr(key);
-      kreg[u] = key < Lk ? load16(k_cache + off + c * 16) : Vec16{{0u, 0u, 0u, 0u}};
+      const int key = kt0 + item / KCH;
+      kreg[u] = key < Lk ? load16(k_cache + row_addr(key) + (item % KCH) * 16) : Vec16{{0u, 0u, 0u, 0u}};
     }
 #pragma unroll
     for (int e = 0; e < VK; ++e) {
-      const int r = vkg * VK + e;
-      const int key = kt0 + r;
-      const int64_t off = tile_in_block ? tile_base + r * row_bytes : row_addr(key);
-      vreg[e] = key < Lk ? load16(v_cache + off + vdc * 16) : Vec16{{0u, 0u, 0u, 0u}};
+      const int key = kt0 + vkg * VK + e;
+      vreg[e] = key < Lk ? load16(v_cache + row_addr(key) + vdc * 16) : Vec16{{0u, 0u, 0u, 0u}};
     }
   };
   auto commit = [&](int buf) {
@@ -254,7 +285,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
     }
 
     const bool need_mask = !(kt0 + kKeys - 1 <= start + q_lo && kt0 + kKeys <= Lk);
-    uint32_t pop[2][2][4];  // [k-step of 32 keys][t][packed pair]
+    Vec16 pop[2][2];  // [k-step of 32 keys][t]: P^T operand, 8 bf16
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       if (need_mask) {
@@ -284,23 +315,25 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
         for (int dt = 0; dt < DT; ++dt) o[dt][t] *= alpha;
       }
       m[t] = m_new;
-      float lsum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = fast_exp2(fmaf(s[kt][t][e], scale_log2, -m_new));
-          s[kt][t][e] = p;
-          lsum += p;
-        }
-      l[t] += lsum;
+        for (int e = 0; e < 4; ++e) s[kt][t][e] = fast_exp2(fmaf(s[kt][t][e], scale_log2, -m_new));
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        pop[st][t][0] = pack2(s[2 * st][t][0], s[2 * st][t][1]);
-        pop[st][t][1] = pack2(s[2 * st][t][2], s[2 * st][t][3]);
-        pop[st][t][2] = pack2(s[2 * st + 1][t][0], s[2 * st + 1][t][1]);
-        pop[st][t][3] = pack2(s[2 * st + 1][t][2], s[2 * st + 1][t][3]);
+        pop[st][t].w[0] = pack2(s[2 * st][t][0], s[2 * st][t][1]);
+        pop[st][t].w[1] = pack2(s[2 * st][t][2], s[2 * st][t][3]);
+        pop[st][t].w[2] = pack2(s[2 * st + 1][t][0], s[2 * st + 1][t][1]);
+        pop[st][t].w[3] = pack2(s[2 * st + 1][t][2], s[2 * st + 1][t][3]);
       }
+      // row sum of the weights as the PV product sees them (bf16), two at a
+      // time with v_dot2 against (1, 1)
+      float lsum = l[t];
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) lsum = dot2_bf16(pop[st][t].w[w], kOnesBf16x2, lsum);
+      l[t] = lsum;
     }
 
     // O^T += V^T P^T
@@ -315,8 +348,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
         const bf16x8_t a = as_bf16x8(va);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const Vec16 pb{{pop[st][t][0], pop[st][t][1], pop[st][t][2], pop[st][t][3]}};
-          o[dt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pb), o[dt][t], 0, 0, 0);
+          o[dt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pop[st][t]), o[dt][t], 0, 0, 0);
         }
       }
     }
