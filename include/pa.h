@@ -162,39 +162,78 @@ pa_status pa_decode(void* out, const void* q, int64_t q_row_stride,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * pa_prefill_varlen - packed varlen causal prefill over a paged cache
- * ("Inference Engine Inside nano-vLLM", "Attention in nano-vLLM", the
- * flash_attn_varlen_func branch with k, v = k_cache, v_cache when a prefix
- * is cached; "nano-vLLM Part 2 ...", sections 2.5 and 4.1; "From nano-vLLM
- * to vLLM ...", sections 8.1-8.3).
+ * pa_store_decode - the decode step's scatter and attention in one launch
+ * (the two calls of Attention.forward in decode: "Inference Engine Inside
+ * nano-vLLM", "Attention in nano-vLLM": store_kvcache, then
+ * flash_attn_with_kvcache; "nano-vLLM Part 2 ...", section 3.1).
+ *
+ * Same result, bit for bit, as pa_store_kvcache(key, value, k_cache,
+ * v_cache, slot_mapping) followed by pa_decode(...) with the same
+ * arguments, under one extra precondition: slot_mapping[b] is -1 or the slot
+ * of logical position context_lens[b] - 1 of sequence b (as the decode
+ * runner builds it), and is -1 whenever context_lens[b] == 0. The partition
+ * that holds that position reads the new row from key / value and writes it
+ * to the caches.
+ *
+ *   key, value    [num_seqs, num_kv_heads, head_dim]; row b at key + b * key_row_stride.
+ *   slot_mapping  int32 [num_seqs].
+ *   k_cache, v_cache  written at the slots, otherwise read only.
+ * Everything else as pa_decode, including the workspace
+ * (pa_decode_workspace_size) and the error codes.
+ */
+pa_status pa_store_decode(void* out, const void* q, int64_t q_row_stride, const void* key,
+                          int64_t key_row_stride, const void* value, int64_t value_row_stride,
+                          const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          int32_t num_blocks, float scale, int32_t partition_size,
+                          pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
+ * pa_prefill_varlen - packed varlen causal prefill ("Inference Engine Inside
+ * nano-vLLM", "Attention in nano-vLLM", the flash_attn_varlen_func branch;
+ * "nano-vLLM Part 2 ...", sections 2.3, 2.5 and 4.1; "From nano-vLLM to
+ * vLLM ...", sections 8.1-8.3).
  *
  * Sequence i owns query rows cu_seqlens_q[i] .. cu_seqlens_q[i+1]-1
- * (Lq of them) and sees Lk = cu_seqlens_k[i+1] - cu_seqlens_k[i] keys: the
- * first Lk logical rows of its block-table row (cached prefix + this step's
- * chunk, which pa_store_kvcache must have written already). Query j
- * (0-based within the sequence) sits at position Lk - Lq + j and attends to
- * keys 0 .. Lk - Lq + j (bottom-right causal alignment):
+ * (Lq of them) and sees Lk = cu_seqlens_k[i+1] - cu_seqlens_k[i] keys.
+ * Query j (0-based within the sequence) sits at position Lk - Lq + j and
+ * attends to keys 0 .. Lk - Lq + j (bottom-right causal alignment):
  *   out[row][h] = softmax(scale * q[row][h] . K_g[0..Lk-Lq+j]^T) V_g[...].
+ *
+ * Where the keys come from depends on block_tables:
+ *   paged (block_tables != NULL): k, v are the caches [num_blocks,
+ *     block_size, num_kv_heads, head_dim]; key t of sequence i is logical row
+ *     t of its block-table row (cached prefix + this step's chunk, which
+ *     pa_store_kvcache must have written already). k_row_stride and
+ *     v_row_stride are 0 or num_kv_heads * head_dim.
+ *   packed (block_tables == NULL): k, v are [total_k, num_kv_heads,
+ *     head_dim] with row strides k_row_stride / v_row_stride (elements, inner
+ *     part contiguous, rows 16-byte aligned); key t of sequence i is row
+ *     cu_seqlens_k[i] + t. This is the no-prefix branch on the pages, where
+ *     attention reads the K/V computed in the same forward pass.
+ *     block_size, num_blocks and max_blocks_per_seq are ignored.
  *
  *   out           [total_q, num_q_heads, head_dim], contiguous.
  *   q             [total_q, num_q_heads, head_dim]; row r at q + r * q_row_stride.
  *   cu_seqlens_q, cu_seqlens_k  int32 [num_seqs + 1], device.
  *   max_seqlen_q  >= every Lq; max_seqlen_k >= every Lk (host integers that
  *                 size the launch, as the pages pass them).
- *   block_tables  int32 [num_seqs, max_blocks_per_seq]. NULL (packed
- *                 contiguous K/V mode) is not built yet: PA_ERR_UNSUPPORTED.
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq] or NULL.
  * Only PA_BF16 is built (the contractions run on bf16 MFMA with fp32
  * accumulation); head_dim 64 or 128; group size 1, 2, 4, 8 or 16; block_size
- * a power of two in [16, 1024].
+ * a power of two in [1, 1024].
  */
 pa_status pa_prefill_varlen(void* out, const void* q, int64_t q_row_stride, int32_t total_q,
-                            const void* k_cache, const void* v_cache,
-                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                            int32_t max_seqlen_q, int32_t max_seqlen_k,
-                            const int32_t* block_tables, int32_t max_blocks_per_seq,
-                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                            int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                            float scale, pa_dtype dtype, void* stream);
+                            const void* k, int64_t k_row_stride, const void* v,
+                            int64_t v_row_stride, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, float scale, pa_dtype dtype, void* stream);
 
 #ifdef __cplusplus
 }

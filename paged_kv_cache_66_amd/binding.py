@@ -39,9 +39,12 @@ _SIGNATURES = {
     "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                  _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _sz, _vp]),
-    "pa_prefill_varlen": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
-                                         _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
-                                         ctypes.c_int, _vp]),
+    "pa_store_decode": (ctypes.c_int, [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i32,
+                                       _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                       ctypes.c_int, _vp, _sz, _vp]),
+    "pa_prefill_varlen": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _i64, _vp, _i64, _vp, _vp, _i32,
+                                         _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                         _f32, ctypes.c_int, _vp]),
 }
 
 
@@ -167,31 +170,78 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None, 
     return out
 
 
-def pa_prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                      block_tables, scale, out=None):
-    """Packed varlen causal prefill through the block tables. q [Tq, H_q, D]."""
+def pa_store_decode(q, key, value, slot_mapping, k_cache, v_cache, block_tables, context_lens, scale,
+                    out=None, workspace=None, partition_size=0):
+    """pa_store_kvcache + pa_decode in one launch. q [B, H_q, D]; key/value
+    [B, H_kv, D]; slot_mapping[b] is -1 or the slot of position
+    context_lens[b] - 1."""
     import torch
     lib = load()
     n, bs, hkv, d = _cache_dims(k_cache, v_cache)
+    _int32(block_tables, "block_tables")
+    _int32(context_lens, "context_lens")
+    _int32(slot_mapping, "slot_mapping")
+    qp, qs = _rows(q, "q")
+    kp, ks = _rows(key, "key")
+    vp, vs = _rows(value, "value")
+    b, hq = int(q.shape[0]), int(q.shape[1])
+    _require(q.shape[2] == d and q.dtype == k_cache.dtype, "q shape/dtype")
+    _require(tuple(key.shape) == (b, hkv, d) and tuple(value.shape) == (b, hkv, d), "key/value shape")
+    _require(key.dtype == value.dtype == k_cache.dtype, "key/value dtype")
+    _require(slot_mapping.shape == (b,), "slot_mapping must be [B]")
+    _require(block_tables.dim() == 2 and block_tables.shape[0] == b, "block_tables must be [B, W]")
+    _require(context_lens.shape == (b,), "context_lens must be [B]")
+    w = int(block_tables.shape[1])
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=q.dtype, device=q.device)
+    _require(out.is_contiguous() and tuple(out.shape) == (b, hq, d) and out.dtype == q.dtype, "out")
+    need = pa_decode_workspace_size(b, hq, hkv, d, bs, w, partition_size) if b > 0 else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wp = workspace.data_ptr() if workspace is not None else None
+    wn = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.pa_store_decode(out.data_ptr(), qp, qs, kp, ks, vp, vs, slot_mapping.data_ptr(),
+                             k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), w,
+                             context_lens.data_ptr(), b, hq, hkv, d, bs, n, float(scale),
+                             int(partition_size), _dtype_code(q), wp, wn, _stream(q))
+    _check("pa_store_decode", st)
+    return out
+
+
+def pa_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                      block_tables, scale, out=None):
+    """Packed varlen causal prefill. q [Tq, H_q, D].
+
+    With block_tables ([B, W] int32) k and v are the paged caches
+    [N, bs, H_kv, D]; with block_tables=None they are packed [Tk, H_kv, D]
+    (row-strided views are fine) and key t of sequence i is row
+    cu_seqlens_k[i] + t."""
+    import torch
+    lib = load()
     _int32(cu_seqlens_q, "cu_seqlens_q")
     _int32(cu_seqlens_k, "cu_seqlens_k")
     qp, qs = _rows(q, "q")
     tq, hq = int(q.shape[0]), int(q.shape[1])
-    _require(q.shape[2] == d and q.dtype == k_cache.dtype, "q shape/dtype")
     bsq = int(cu_seqlens_q.shape[0]) - 1
     _require(cu_seqlens_k.shape == cu_seqlens_q.shape, "cu_seqlens_k must match cu_seqlens_q")
     if block_tables is not None:
+        n, bs, hkv, d = _cache_dims(k, v)
         _int32(block_tables, "block_tables")
         _require(block_tables.dim() == 2 and block_tables.shape[0] == bsq, "block_tables must be [B, W]")
         bt_ptr, w = block_tables.data_ptr(), int(block_tables.shape[1])
+        kp, ks, vp, vs = k.data_ptr(), 0, v.data_ptr(), 0
     else:
-        bt_ptr, w = None, 0
+        kp, ks = _rows(k, "k")
+        vp, vs = _rows(v, "v")
+        hkv, d = int(k.shape[1]), int(k.shape[2])
+        _require(tuple(v.shape[1:]) == (hkv, d) and v.dtype == k.dtype, "k/v shapes")
+        n, bs, bt_ptr, w = 0, 0, None, 0
+    _require(q.shape[2] == d and q.dtype == k.dtype, "q shape/dtype")
     if out is None:
         out = torch.empty((tq, hq, d), dtype=q.dtype, device=q.device)
     _require(out.is_contiguous() and tuple(out.shape) == (tq, hq, d) and out.dtype == q.dtype, "out")
-    st = lib.pa_prefill_varlen(out.data_ptr(), qp, qs, tq, k_cache.data_ptr(), v_cache.data_ptr(),
-                               cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), int(max_seqlen_q),
-                               int(max_seqlen_k), bt_ptr, w, bsq, hq, hkv, d, bs, n, float(scale),
-                               _dtype_code(q), _stream(q))
+    st = lib.pa_prefill_varlen(out.data_ptr(), qp, qs, tq, kp, ks, vp, vs, cu_seqlens_q.data_ptr(),
+                               cu_seqlens_k.data_ptr(), int(max_seqlen_q), int(max_seqlen_k), bt_ptr, w,
+                               bsq, hq, hkv, d, bs, n, float(scale), _dtype_code(q), _stream(q))
     _check("pa_prefill_varlen", st)
     return out

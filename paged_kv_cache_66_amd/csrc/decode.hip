@@ -135,14 +135,23 @@ template <> struct QSlice<BF16Tag> {
 // Dynamic LDS layout of the partition kernel (in 4-byte words):
 //   [0, G * max(partition, 4 * D))   scores, then reused for the wave reduction
 //   then G maxima, G sums, then the partition's block ids.
-template <typename T, int D, int G>
+//
+// With FUSED the step's new K/V rows are scattered by this kernel as well
+// (one launch instead of pa_store_kvcache + pa_decode): the workgroup whose
+// partition holds position context_len - 1 of a sequence reads that row from
+// the new key/value inputs instead of the cache and writes its kv head slice
+// to the cache at slot_mapping[b]. The caller guarantees that slot is the
+// slot of position context_len - 1 (or -1: no store, row read from the cache).
+template <typename T, int D, int G, bool FUSED>
 __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
     void* __restrict__ out, const char* __restrict__ q, int64_t q_stride_bytes,
-    const char* __restrict__ k_cache, const char* __restrict__ v_cache,
+    char* __restrict__ k_cache, char* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, int32_t max_blocks,
     const int32_t* __restrict__ context_lens, int32_t num_q_heads, int32_t num_kv_heads,
     int32_t log2_bs, float scale_log2, int32_t partition, int32_t num_partitions,
-    int32_t score_words, float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
+    int32_t score_words, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+    const char* __restrict__ new_k, int64_t new_k_stride_bytes, const char* __restrict__ new_v,
+    int64_t new_v_stride_bytes, const int32_t* __restrict__ slot_mapping) {
   using E = Elem<T>;
   constexpr int EPV = E::kPerVec;    // elements per 16-byte vector
   constexpr int EB = E::kBytes;      // bytes per element
@@ -229,6 +238,21 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
     return static_cast<uint64_t>((blk << log2_bs) + (pos & bs_mask)) * row_bytes;
   };
 
+  // the step's new row: local index in this partition (-1: not here / no store)
+  int new_tl = -1;
+  const char* nk_row = nullptr;
+  const char* nv_row = nullptr;
+  int64_t new_dst = 0;
+  if constexpr (FUSED) {
+    const int slot = slot_mapping[b];
+    if (slot >= 0 && n - 1 >= t0 && n - 1 < t1) {
+      new_tl = n - 1 - t0;
+      nk_row = new_k + static_cast<int64_t>(b) * new_k_stride_bytes + static_cast<int64_t>(g) * D * EB;
+      nv_row = new_v + static_cast<int64_t>(b) * new_v_stride_bytes + static_cast<int64_t>(g) * D * EB;
+      new_dst = static_cast<int64_t>(slot) * static_cast<int64_t>(row_bytes) + static_cast<int64_t>(g) * D * EB;
+    }
+  }
+
   // phase 1: raw scores q . k (the scale is applied once per score in phase 2)
   const char* kbase1 = k_cache + static_cast<int64_t>(g) * D * EB + li1 * 16;
   const int my_row1 = wave * TPW1 + grp1;
@@ -237,7 +261,13 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int tl = base + u * STEP1 + my_row1;
-      if (tl < ntok) {
+      if (FUSED && tl == new_tl) {
+        // new row: from the inputs, and written to its cache slot
+        k0[u] = load16(nk_row + li1 * 16);
+        k1[u] = load16(nk_row + (LPT1 + li1) * 16);
+        store16(k_cache + new_dst + li1 * 16, k0[u]);
+        store16(k_cache + new_dst + (LPT1 + li1) * 16, k1[u]);
+      } else if (tl < ntok) {
         const char* r = kbase1 + row_off(tl);
         k0[u] = load16_nt(r);
         k1[u] = load16_nt(r + LPT1 * 16);
@@ -293,7 +323,12 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int tl = base + u * STEP + my_row;
-      vv[u] = tl < ntok ? load16_nt(vbase + row_off(tl)) : Vec16{{0u, 0u, 0u, 0u}};
+      if (FUSED && tl == new_tl) {
+        vv[u] = load16(nv_row + li * 16);
+        store16(v_cache + new_dst + li * 16, vv[u]);
+      } else {
+        vv[u] = tl < ntok ? load16_nt(vbase + row_off(tl)) : Vec16{{0u, 0u, 0u, 0u}};
+      }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -418,7 +453,7 @@ __global__ void __launch_bounds__(64) decode_reduce_kernel(
   }
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool FUSED>
 hipError_t launch_decode_typed(const DecodeArgs& a, hipStream_t stream) {
   constexpr int EB = Elem<T>::kBytes;
   int log2_bs = 0;
@@ -428,12 +463,14 @@ hipError_t launch_decode_typed(const DecodeArgs& a, hipStream_t stream) {
   const size_t lds = static_cast<size_t>(score_words + 2 * G + max_ids) * 4;
   const float scale_log2 = a.scale * kLog2e;
   dim3 grid(a.num_partitions * a.num_kv_heads * a.num_seqs);
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, G>), grid, dim3(kThreads), lds, stream, a.out,
-                     static_cast<const char*>(a.q), a.q_stride * EB,
-                     static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache),
-                     a.block_tables, a.max_blocks, a.context_lens, a.num_q_heads, a.num_kv_heads,
-                     log2_bs, scale_log2, a.partition, a.num_partitions, score_words, a.ws_acc,
-                     a.ws_ml);
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, G, FUSED>), grid, dim3(kThreads), lds, stream,
+                     a.out, static_cast<const char*>(a.q), a.q_stride * EB,
+                     static_cast<char*>(const_cast<void*>(a.k_cache)),
+                     static_cast<char*>(const_cast<void*>(a.v_cache)), a.block_tables, a.max_blocks,
+                     a.context_lens, a.num_q_heads, a.num_kv_heads, log2_bs, scale_log2, a.partition,
+                     a.num_partitions, score_words, a.ws_acc, a.ws_ml,
+                     static_cast<const char*>(a.new_k), a.new_k_stride * EB,
+                     static_cast<const char*>(a.new_v), a.new_v_stride * EB, a.slot_mapping);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.num_partitions == 1) return err;
   hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3(a.num_q_heads, a.num_seqs), dim3(64), 0,
@@ -442,16 +479,22 @@ hipError_t launch_decode_typed(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool FUSED>
 hipError_t dispatch_group(const DecodeArgs& a, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_decode_typed<T, D, 1>(a, stream);
-    case 2: return launch_decode_typed<T, D, 2>(a, stream);
-    case 4: return launch_decode_typed<T, D, 4>(a, stream);
-    case 8: return launch_decode_typed<T, D, 8>(a, stream);
-    case 16: return launch_decode_typed<T, D, 16>(a, stream);
+    case 1: return launch_decode_typed<T, D, 1, FUSED>(a, stream);
+    case 2: return launch_decode_typed<T, D, 2, FUSED>(a, stream);
+    case 4: return launch_decode_typed<T, D, 4, FUSED>(a, stream);
+    case 8: return launch_decode_typed<T, D, 8, FUSED>(a, stream);
+    case 16: return launch_decode_typed<T, D, 16, FUSED>(a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <typename T, int D>
+hipError_t dispatch_fused(const DecodeArgs& a, hipStream_t stream) {
+  return a.slot_mapping != nullptr ? dispatch_group<T, D, true>(a, stream)
+                                   : dispatch_group<T, D, false>(a, stream);
 }
 
 }  // namespace
@@ -474,11 +517,11 @@ int32_t decode_partition_tokens(int32_t requested, int32_t num_seqs, int32_t num
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.bf16) {
-    return a.head_dim == 64 ? dispatch_group<BF16Tag, 64>(a, stream)
-                            : dispatch_group<BF16Tag, 128>(a, stream);
+    return a.head_dim == 64 ? dispatch_fused<BF16Tag, 64>(a, stream)
+                            : dispatch_fused<BF16Tag, 128>(a, stream);
   }
-  return a.head_dim == 64 ? dispatch_group<float, 64>(a, stream)
-                          : dispatch_group<float, 128>(a, stream);
+  return a.head_dim == 64 ? dispatch_fused<float, 64>(a, stream)
+                          : dispatch_fused<float, 128>(a, stream);
 }
 
 }  // namespace pa

@@ -111,12 +111,16 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
   return static_cast<size_t>(slots * head_dim * 4 + slots * 2 * 4);
 }
 
-pa_status pa_decode(void* out, const void* q, int64_t q_row_stride, const void* k_cache,
-                    const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                    float scale, int32_t partition_size, pa_dtype dtype, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+namespace {
+
+// Validation and argument packing shared by pa_decode and pa_store_decode.
+pa_status prepare_decode(void* out, const void* q, int64_t q_row_stride, const void* k_cache,
+                         const void* v_cache, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                         int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                         int32_t partition_size, pa_dtype dtype, void* workspace,
+                         size_t workspace_bytes, pa::DecodeArgs* a) {
   if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0)
     return PA_ERR_SHAPE;
@@ -152,31 +156,77 @@ pa_status pa_decode(void* out, const void* q, int64_t q_row_stride, const void* 
     ws_acc = static_cast<float*>(workspace);
     ws_ml = ws_acc + static_cast<int64_t>(num_seqs) * num_q_heads * P * head_dim;
   }
-  pa::DecodeArgs a{};
-  a.out = out;
-  a.q = q;
-  a.q_stride = q_row_stride;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_tables = block_tables;
-  a.max_blocks = max_blocks_per_seq;
-  a.context_lens = context_lens;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.head_dim = head_dim;
-  a.block_size = block_size;
-  a.scale = scale;
-  a.partition = part;
-  a.num_partitions = static_cast<int32_t>(P);
-  a.ws_acc = ws_acc;
-  a.ws_ml = ws_ml;
-  a.bf16 = dtype == PA_BF16;
+  *a = pa::DecodeArgs{};
+  a->out = out;
+  a->q = q;
+  a->q_stride = q_row_stride;
+  a->k_cache = k_cache;
+  a->v_cache = v_cache;
+  a->block_tables = block_tables;
+  a->max_blocks = max_blocks_per_seq;
+  a->context_lens = context_lens;
+  a->num_seqs = num_seqs;
+  a->num_q_heads = num_q_heads;
+  a->num_kv_heads = num_kv_heads;
+  a->head_dim = head_dim;
+  a->block_size = block_size;
+  a->scale = scale;
+  a->partition = part;
+  a->num_partitions = static_cast<int32_t>(P);
+  a->ws_acc = ws_acc;
+  a->ws_ml = ws_ml;
+  a->bf16 = dtype == PA_BF16;
+  return PA_OK;
+}
+
+}  // namespace
+
+pa_status pa_decode(void* out, const void* q, int64_t q_row_stride, const void* k_cache,
+                    const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                    float scale, int32_t partition_size, pa_dtype dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  pa::DecodeArgs a;
+  pa_status st = prepare_decode(out, q, q_row_stride, k_cache, v_cache, block_tables,
+                                max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                                num_kv_heads, head_dim, block_size, num_blocks, scale,
+                                partition_size, dtype, workspace, workspace_bytes, &a);
+  if (st != PA_OK || num_seqs == 0) return st;
+  return pa::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_store_decode(void* out, const void* q, int64_t q_row_stride, const void* key,
+                          int64_t key_row_stride, const void* value, int64_t value_row_stride,
+                          const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          int32_t num_blocks, float scale, int32_t partition_size,
+                          pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  pa::DecodeArgs a;
+  pa_status st = prepare_decode(out, q, q_row_stride, k_cache, v_cache, block_tables,
+                                max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                                num_kv_heads, head_dim, block_size, num_blocks, scale,
+                                partition_size, dtype, workspace, workspace_bytes, &a);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (key == nullptr || value == nullptr || slot_mapping == nullptr) return PA_ERR_NULL;
+  const int eb = elem_bytes(dtype);
+  const int64_t row = static_cast<int64_t>(num_kv_heads) * head_dim;
+  if ((st = check_rows(key, key_row_stride, row, eb)) != PA_OK) return st;
+  if ((st = check_rows(value, value_row_stride, row, eb)) != PA_OK) return st;
+  a.new_k = key;
+  a.new_k_stride = key_row_stride;
+  a.new_v = value;
+  a.new_v_stride = value_row_stride;
+  a.slot_mapping = slot_mapping;
   return pa::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 pa_status pa_prefill_varlen(void* out, const void* q, int64_t q_row_stride, int32_t total_q,
-                            const void* k_cache, const void* v_cache, const int32_t* cu_seqlens_q,
+                            const void* k, int64_t k_row_stride, const void* v,
+                            int64_t v_row_stride, const int32_t* cu_seqlens_q,
                             const int32_t* cu_seqlens_k, int32_t max_seqlen_q,
                             int32_t max_seqlen_k, const int32_t* block_tables,
                             int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
@@ -191,17 +241,30 @@ pa_status pa_prefill_varlen(void* out, const void* q, int64_t q_row_stride, int3
   const int32_t G = num_q_heads / num_kv_heads;
   if (!group_ok(G)) return PA_ERR_UNSUPPORTED;
   if (num_seqs > kMaxGridYZ || num_kv_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
-  pa_status st = check_head_layout(head_dim, block_size, num_blocks);
-  if (st != PA_OK) return st;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale) || !(scale > 0.f)) return PA_ERR_SHAPE;
-  if (block_tables == nullptr) return PA_ERR_UNSUPPORTED;  // packed contiguous mode not built
-  if (max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  const int64_t row = static_cast<int64_t>(num_kv_heads) * head_dim;
+  const bool paged = block_tables != nullptr;
+  pa_status st;
+  if (paged) {
+    if ((st = check_head_layout(head_dim, block_size, num_blocks)) != PA_OK) return st;
+    if (max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+    // the caches are contiguous: a row stride, if given, must say so
+    if ((k_row_stride != 0 && k_row_stride != row) || (v_row_stride != 0 && v_row_stride != row))
+      return PA_ERR_SHAPE;
+    k_row_stride = v_row_stride = row;
+  } else {
+    // packed rows: a tile of 64 rows must stay addressable with 32-bit offsets
+    if (k_row_stride < row || v_row_stride < row) return PA_ERR_SHAPE;
+    if (k_row_stride > (INT32_MAX / 2) / 64 || v_row_stride > (INT32_MAX / 2) / 64) return PA_ERR_SHAPE;
+    if ((k_row_stride * 2) % 16 != 0 || (v_row_stride * 2) % 16 != 0) return PA_ERR_ALIGN;
+  }
   if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PA_OK;
-  if (out == nullptr || q == nullptr || k_cache == nullptr || v_cache == nullptr ||
-      cu_seqlens_q == nullptr || cu_seqlens_k == nullptr)
+  if (out == nullptr || q == nullptr || k == nullptr || v == nullptr || cu_seqlens_q == nullptr ||
+      cu_seqlens_k == nullptr)
     return PA_ERR_NULL;
   const int eb = elem_bytes(dtype);
-  if (!aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
+  if (!aligned16(out) || !aligned16(k) || !aligned16(v)) return PA_ERR_ALIGN;
   if ((st = check_rows(q, q_row_stride, static_cast<int64_t>(num_q_heads) * head_dim, eb)) != PA_OK)
     return st;
   pa::PrefillArgs a{};
@@ -209,19 +272,21 @@ pa_status pa_prefill_varlen(void* out, const void* q, int64_t q_row_stride, int3
   a.q = q;
   a.q_stride = q_row_stride;
   a.total_q = total_q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
+  a.k_cache = k;
+  a.v_cache = v;
+  a.k_stride = k_row_stride;
+  a.v_stride = v_row_stride;
   a.cu_q = cu_seqlens_q;
   a.cu_k = cu_seqlens_k;
   a.max_seqlen_q = max_seqlen_q;
   a.max_seqlen_k = max_seqlen_k;
   a.block_tables = block_tables;
-  a.max_blocks = max_blocks_per_seq;
+  a.max_blocks = paged ? max_blocks_per_seq : 0;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
-  a.block_size = block_size;
+  a.block_size = paged ? block_size : 1;
   a.scale = scale;
   return pa::launch_prefill(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

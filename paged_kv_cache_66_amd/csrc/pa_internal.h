@@ -42,6 +42,12 @@ struct DecodeArgs {
   float* ws_acc;         // [B, H_q, P, D] when num_partitions > 1
   float* ws_ml;          // [B, H_q, P, 2]
   bool bf16;
+  // fused scatter of the step's new rows (slot_mapping == nullptr: plain decode)
+  const void* new_k;
+  int64_t new_k_stride;  // elements
+  const void* new_v;
+  int64_t new_v_stride;
+  const int32_t* slot_mapping;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
@@ -51,8 +57,10 @@ struct PrefillArgs {
   const void* q;
   int64_t q_stride;  // elements
   int32_t total_q;
-  const void* k_cache;
+  const void* k_cache;  // caches (paged) or packed k rows (block_tables == nullptr)
   const void* v_cache;
+  int64_t k_stride;  // elements between key rows: H_kv * D for the caches
+  int64_t v_stride;
   const int32_t* cu_q;
   const int32_t* cu_k;
   int32_t max_seqlen_q;

@@ -77,8 +77,8 @@ __device__ __forceinline__ uint32_t half16(const Vec16& v, int j) {
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
     uint16_t* __restrict__ out, const char* __restrict__ q, int64_t q_stride_bytes,
-    const char* __restrict__ k_cache, const char* __restrict__ v_cache,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+    const char* __restrict__ k_cache, const char* __restrict__ v_cache, int64_t k_stride_bytes,
+    int64_t v_stride_bytes, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
     const int32_t* __restrict__ block_tables, int32_t max_blocks, int32_t num_q_heads,
     int32_t num_kv_heads, int32_t log2_bs, float scale_log2, int32_t max_qt) {
   constexpr int QT = kRows / G;    // queries per workgroup
@@ -161,18 +161,23 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
     }
   }
 
-  const int64_t row_bytes = static_cast<int64_t>(num_kv_heads) * D * 2;
+  // Key rows come either from the paged caches (row stride H_kv * D) through
+  // the block table, or, without a table, from packed k / v tensors where key
+  // t of sequence i is row cu_k[i] + t (row strides given by the caller).
+  const bool paged = block_tables != nullptr;
   const int64_t head_off = static_cast<int64_t>(g) * D * 2;
-  const int32_t* table = block_tables + static_cast<int64_t>(i) * max_blocks;
+  const int32_t* table = paged ? block_tables + static_cast<int64_t>(i) * max_blocks : nullptr;
   const int bs_mask = (1 << log2_bs) - 1;
+  const int64_t k0_row = paged ? 0 : cu_k[i];
 
-  // Byte offset of key row `key` of this sequence (kv head slice included).
+  // Byte offset of key row `key` in the paged caches (kv head slice included).
   // With blocks of at least one tile (64 keys) a tile lies inside one block,
   // so its block id is read once per tile; smaller blocks look up every row.
-  const bool tile_in_block = log2_bs >= 6;
+  // Packed rows are always contiguous.
+  const bool tile_contiguous = !paged || log2_bs >= 6;
   auto row_addr = [&](int key) -> int64_t {
     const int64_t blk = table[key >> log2_bs];
-    return ((blk << log2_bs) + (key & bs_mask)) * row_bytes + head_off;
+    return ((blk << log2_bs) + (key & bs_mask)) * k_stride_bytes + head_off;
   };
 
   // ---- tile fetch into registers ----
@@ -180,23 +185,25 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   Vec16 vreg[VK];
   const int vkg = tid % VGROUPS;  // group of VK consecutive V rows of the item
   const int vdc = tid / VGROUPS;  // 16-byte chunk of the V item
-  // Byte offsets of this thread's K and V vectors inside a tile that lies in
-  // one block (rows x row size + chunk: under 2^31 for any supported shape);
-  // fixed for the whole kernel, so a tile fetch adds one uniform base.
+  // Byte offsets of this thread's K and V vectors inside a contiguous tile
+  // (rows x row stride + chunk: under 2^31 for any supported shape); fixed for
+  // the whole kernel, so a tile fetch adds one uniform base.
   uint32_t koff[KLOADS];
   uint32_t voff[VK];
 #pragma unroll
   for (int u = 0; u < KLOADS; ++u) {
     const int item = tid + u * kThreads;
-    koff[u] = static_cast<uint32_t>((item / KCH) * row_bytes + (item % KCH) * 16);
+    koff[u] = static_cast<uint32_t>((item / KCH) * k_stride_bytes + (item % KCH) * 16);
   }
 #pragma unroll
-  for (int e = 0; e < VK; ++e) voff[e] = static_cast<uint32_t>((vkg * VK + e) * row_bytes + vdc * 16);
+  for (int e = 0; e < VK; ++e)
+    voff[e] = static_cast<uint32_t>((vkg * VK + e) * v_stride_bytes + vdc * 16);
 
   auto fetch = [&](int kt0) {
-    if (tile_in_block) {
-      const char* kb = k_cache + row_addr(kt0);  // kt0 < Lk always
-      const char* vb = v_cache + row_addr(kt0);
+    if (tile_contiguous) {
+      // kt0 < Lk always, so the tile's first row exists
+      const char* kb = paged ? k_cache + row_addr(kt0) : k_cache + (k0_row + kt0) * k_stride_bytes + head_off;
+      const char* vb = paged ? v_cache + row_addr(kt0) : v_cache + (k0_row + kt0) * v_stride_bytes + head_off;
 #pragma unroll
       for (int u = 0; u < KLOADS; ++u) {
         const int key = kt0 + (tid + u * kThreads) / KCH;
@@ -387,7 +394,8 @@ hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
   dim3 grid(static_cast<uint32_t>(total));
   hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(kThreads), 0, stream,
                      static_cast<uint16_t*>(a.out), static_cast<const char*>(a.q), a.q_stride * 2,
-                     static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache), a.cu_q,
+                     static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache),
+                     a.k_stride * 2, a.v_stride * 2, a.cu_q,
                      a.cu_k, a.block_tables, a.max_blocks, a.num_q_heads, a.num_kv_heads, log2_bs,
                      a.scale * kLog2e, max_qt);
   return hipGetLastError();

@@ -25,7 +25,8 @@ def lib():
 def test_exports_every_header_symbol(lib):
     names = binding.header_symbols()
     assert set(names) == {"pa_status_string", "pa_version", "pa_store_kvcache",
-                          "pa_decode_workspace_size", "pa_decode", "pa_prefill_varlen"}
+                          "pa_decode_workspace_size", "pa_decode", "pa_store_decode",
+                          "pa_prefill_varlen"}
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -107,20 +108,41 @@ def test_decode_validation(lib):
     assert lib.pa_decode_workspace_size(4, 4, 2, 64, 16, 4, 64) == 0  # one partition of 64
 
 
-def prefill(lib, **kw):
-    a = dict(out=A, q=A, qs=512, tq=8, kc=A, vc=A, cuq=A, cuk=A, mq=8, mk=8, bt=A, w=4, b=1, hq=4,
-             hkv=2, d=128, bs=16, n=32, scale=0.1, dtype=BF16)
+def store_decode(lib, **kw):
+    a = dict(out=A, q=A, qs=256, key=A, ks=128, value=A, vs=128, slots=A, kc=A, vc=A, bt=A, w=4, ctx=A,
+             b=4, hq=4, hkv=2, d=64, bs=16, n=32, scale=0.125, part=0, dtype=F32, ws=None, wsn=0)
     a.update(kw)
-    return lib.pa_prefill_varlen(a["out"], a["q"], a["qs"], a["tq"], a["kc"], a["vc"], a["cuq"],
-                                 a["cuk"], a["mq"], a["mk"], a["bt"], a["w"], a["b"], a["hq"], a["hkv"],
-                                 a["d"], a["bs"], a["n"], a["scale"], a["dtype"], None)
+    return lib.pa_store_decode(a["out"], a["q"], a["qs"], a["key"], a["ks"], a["value"], a["vs"],
+                               a["slots"], a["kc"], a["vc"], a["bt"], a["w"], a["ctx"], a["b"], a["hq"],
+                               a["hkv"], a["d"], a["bs"], a["n"], a["scale"], a["part"], a["dtype"],
+                               a["ws"], a["wsn"], None)
+
+
+def test_store_decode_validation(lib):
+    assert store_decode(lib, b=0, out=None, key=None) == OK
+    assert store_decode(lib, key=None) == NULL
+    assert store_decode(lib, slots=None) == NULL
+    assert store_decode(lib, out=None) == NULL
+    assert store_decode(lib, ks=100) == SHAPE
+    assert store_decode(lib, vs=130) == ALIGN
+    assert store_decode(lib, value=A + 4) == ALIGN
+    assert store_decode(lib, hq=6, hkv=2) == UNSUP
+    assert store_decode(lib, w=128) == WS
+
+
+def prefill(lib, **kw):
+    a = dict(out=A, q=A, qs=512, tq=8, k=A, ks=0, v=A, vs=0, cuq=A, cuk=A, mq=8, mk=8, bt=A, w=4, b=1,
+             hq=4, hkv=2, d=128, bs=16, n=32, scale=0.1, dtype=BF16)
+    a.update(kw)
+    return lib.pa_prefill_varlen(a["out"], a["q"], a["qs"], a["tq"], a["k"], a["ks"], a["v"], a["vs"],
+                                 a["cuq"], a["cuk"], a["mq"], a["mk"], a["bt"], a["w"], a["b"], a["hq"],
+                                 a["hkv"], a["d"], a["bs"], a["n"], a["scale"], a["dtype"], None)
 
 
 def test_prefill_validation(lib):
     assert prefill(lib, b=0) == OK
     assert prefill(lib, tq=0) == OK
     assert prefill(lib, dtype=F32) == UNSUP      # only bf16 MFMA path is built
-    assert prefill(lib, bt=None) == UNSUP        # packed contiguous mode not built yet
     assert prefill(lib, cuq=None) == NULL
     assert prefill(lib, hq=5) == SHAPE
     assert prefill(lib, d=32) == UNSUP
@@ -129,6 +151,17 @@ def test_prefill_validation(lib):
     assert prefill(lib, mq=-1) == SHAPE
     assert prefill(lib, scale=0.0) == SHAPE
     assert prefill(lib, scale=float("nan")) == SHAPE
+    # paged mode: the caches are contiguous, a row stride must say so
+    assert prefill(lib, ks=300) == SHAPE
+    assert prefill(lib, bs=24) == UNSUP
+    # packed mode (no block table): row strides required, block size ignored
+    packed = dict(bt=None, w=0, bs=0, n=0, ks=256, vs=256)
+    assert prefill(lib, **{**packed, "tq": 0}) == OK
+    assert prefill(lib, **{**packed, "ks": 0}) == SHAPE
+    assert prefill(lib, **{**packed, "vs": 100}) == SHAPE
+    assert prefill(lib, **{**packed, "ks": 260}) == ALIGN
+    assert prefill(lib, **{**packed, "k": A + 8}) == ALIGN
+    assert prefill(lib, **{**packed, "ks": 1 << 26}) == SHAPE
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

@@ -249,3 +249,57 @@ def test_full_long_context_decode():
     torch.cuda.synchronize()
     diff = (out.float() - out2.float()).abs().max().item()
     assert diff <= 1.5e-2, diff
+
+
+# ---------------------------------------------------------------------------
+# fused scatter + decode (pa_store_decode) == pa_store_kvcache + pa_decode
+# ---------------------------------------------------------------------------
+
+def _fused_vs_separate(w, dev_tensors, partition=0):
+    import torch
+    t = dev_tensors
+    slots = torch.from_numpy(w.slot_mapping).cuda()
+    tables = torch.from_numpy(w.block_tables).cuda()
+    ctx = torch.from_numpy(w.context_lens).cuda()
+    kc2, vc2 = t["k_cache"].clone(), t["v_cache"].clone()
+    print(f"[store-decode] {w.name} B={w.num_seqs} G={w.num_q_heads // w.num_kv_heads} "
+          f"D={w.head_dim} dtype={w.dtype} part={partition}", flush=True)
+    binding.pa_store_kvcache(t["k"], t["v"], t["k_cache"], t["v_cache"], slots)
+    sep = binding.pa_decode(t["q"], t["k_cache"], t["v_cache"], tables, ctx, w.scale,
+                            partition_size=partition)
+    fused = binding.pa_store_decode(t["q"], t["k"], t["v"], slots, kc2, vc2, tables, ctx, w.scale,
+                                    partition_size=partition)
+    torch.cuda.synchronize()
+    iv = torch.int16 if w.dtype == "bf16" else torch.int32
+    assert torch.equal(sep.view(iv), fused.view(iv)), "fused output differs"
+    assert torch.equal(t["k_cache"].view(iv), kc2.view(iv)), "fused K scatter differs"
+    assert torch.equal(t["v_cache"].view(iv), vc2.view(iv)), "fused V scatter differs"
+    return fused
+
+
+@pytest.mark.parametrize("partition", [0, 64])
+@pytest.mark.parametrize("g", [1, 2, 8])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128), ("bf16", 64)])
+def test_store_decode_matches_separate_calls(dtype, d, g, partition):
+    import torch
+    hkv = 2
+    ctx = [1, 15, 16, 17, 33, 100, 257, 64, 65, 0]
+    w = wl.custom_decode(ctx, block_size=16, num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d,
+                         dtype=dtype, seed=3 * g + d, width=20)
+    t = wl.make_host_tensors(w)
+    dev = _device_inputs(w, t)
+    fused = _fused_vs_separate(w, {"q": dev["q"], "k": dev["k"], "v": dev["v"],
+                                   "k_cache": dev["k_cache"], "v_cache": dev["v_cache"]}, partition)
+    kc, vc = t["k_cache"].copy(), t["v_cache"].copy()
+    oracle.store_kvcache(t["k"], t["v"], kc, vc, w.slot_mapping)
+    ref = oracle.decode(t["q"], kc, vc, w.block_tables, w.context_lens, w.scale, w.dtype)
+    assert_attention_close(widen_host(to_host(fused, w.dtype), w.dtype), ref, w.dtype, "fused")
+
+
+@pytest.mark.parametrize("name", ["qwen3-0.6b-decode", "long-context-decode"])
+def test_store_decode_full_size(name):
+    import torch
+    w = wl.DECODE_CONFIGS[name](0)
+    t = wl.make_device_tensors(w)
+    out = _fused_vs_separate(w, t)
+    assert bool(torch.isfinite(out.float()).all())

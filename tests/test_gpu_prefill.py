@@ -119,3 +119,70 @@ def test_full_chunked_prefill_sampled():
     got = widen_host(to_host(out, w.dtype), w.dtype)
     err = assert_attention_close(got[rows], ref[rows], w.dtype, "chunked-prefill sampled rows")
     print(f"[prefill-full] {len(rows)} sampled rows, max err {err:.3e}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# packed K/V mode (no block table): the no-prefix branch of the same call
+# ---------------------------------------------------------------------------
+
+def run_packed(cached, sched, hq, hkv, d, seed):
+    import torch
+    rng = np.random.default_rng(seed)
+    _, cuq, cuk, mq, mk = wl.prefill_layout(cached, sched)
+    tq, tk = int(cuq[-1]), int(cuk[-1])
+    q = wl.randn_storage(rng, (tq, hq, d), "bf16")
+    kv = wl.randn_storage(rng, (tk, 2 * hkv * d + 8), "bf16")  # fused buffer: row-strided k and v
+    k = kv[:, : hkv * d].reshape(tk, hkv, d)
+    v = kv[:, hkv * d: 2 * hkv * d].reshape(tk, hkv, d)
+    scale = 1.0 / np.sqrt(d)
+    print(f"[prefill-packed] cached={cached} sched={sched} Hq={hq} Hkv={hkv} D={d}", flush=True)
+    kv_d = to_device(kv, "bf16")
+    k_d = kv_d[:, : hkv * d].view(tk, hkv, d)
+    v_d = kv_d[:, hkv * d: 2 * hkv * d].view(tk, hkv, d)
+    out = binding.pa_prefill_varlen(to_device(q, "bf16"), k_d, v_d, torch.from_numpy(cuq).cuda(),
+                                    torch.from_numpy(cuk).cuda(), mq, mk, None, scale)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_varlen(q, None, None, cuq, cuk, None, scale, "bf16", k=k, v=v)
+    return assert_attention_close(widen_host(to_host(out, "bf16"), "bf16"), ref, "bf16", "packed")
+
+
+@pytest.mark.parametrize("g", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_packed_no_prefix(g, d):
+    hkv = 2 if g <= 8 else 1
+    sched = [1, 70, 129, 5, 300]
+    run_packed([0] * len(sched), sched, g * hkv, hkv, d, seed=g + d)
+
+
+def test_prefill_packed_with_prefix_rows():
+    # packed keys may also carry earlier rows (Lk > Lq): bottom-right alignment
+    run_packed([3, 0, 64, 200], [50, 17, 64, 1], 32, 8, 128, seed=7)
+
+
+def test_prefill_paged_and_packed_bitwise_equal():
+    """Same keys laid out paged (block size 64) and packed give bit-identical
+    results: the tiles and the arithmetic order depend only on logical rows."""
+    import torch
+    w = wl.custom_prefill([0, 64, 10], [100, 65, 200], block_size=64, num_q_heads=16, num_kv_heads=4,
+                          head_dim=128, dtype="bf16", seed=21)
+    t = wl.make_host_tensors(w)
+    kc, vc = t["k_cache"].copy(), t["v_cache"].copy()
+    oracle.store_kvcache(t["k"], t["v"], kc, vc, w.slot_mapping)
+    # gather each sequence's Lk rows into packed buffers (test-side setup)
+    rows_k, rows_v = [], []
+    for i in range(w.num_seqs):
+        n = int(w.cu_seqlens_k[i + 1] - w.cu_seqlens_k[i])
+        ids = w.block_tables[i, : wl.num_blocks_for(n, w.block_size)]
+        rows_k.append(kc[ids].reshape(-1, w.num_kv_heads, w.head_dim)[:n])
+        rows_v.append(vc[ids].reshape(-1, w.num_kv_heads, w.head_dim)[:n])
+    pk, pv = np.concatenate(rows_k), np.concatenate(rows_v)
+    q_d = to_device(np.ascontiguousarray(t["q"]), "bf16")
+    cuq, cuk = torch.from_numpy(w.cu_seqlens_q).cuda(), torch.from_numpy(w.cu_seqlens_k).cuda()
+    print("[prefill-paged-vs-packed]", flush=True)
+    paged = binding.pa_prefill_varlen(q_d, to_device(kc, "bf16"), to_device(vc, "bf16"), cuq, cuk,
+                                      w.max_seqlen_q, w.max_seqlen_k,
+                                      torch.from_numpy(w.block_tables).cuda(), w.scale)
+    packed = binding.pa_prefill_varlen(q_d, to_device(pk, "bf16"), to_device(pv, "bf16"), cuq, cuk,
+                                       w.max_seqlen_q, w.max_seqlen_k, None, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(paged.view(torch.int16), packed.view(torch.int16))
