@@ -133,12 +133,24 @@ def run_decode(torch, binding, wl, w, steps, warmup, flush, scratch, partition=0
     dec_ms = timer.span(1, 2)
     store_ms = timer.span(0, 1)
     assert bool(torch.isfinite(out.float()).all()), f"{w.name}: non-finite decode output"
+    # the same step as one launch (pa_store_decode)
+    ftimer = Timer(torch, steps, 2)
+    for s in range(steps):
+        if flush:
+            flush_caches(scratch)
+        ftimer.rec(s, 0)
+        binding.pa_store_decode(t["q"], t["k"], t["v"], slots, t["k_cache"], t["v_cache"], tables, ctx,
+                                w.scale, out=out, workspace=ws, partition_size=partition)
+        ftimer.rec(s, 1)
+    torch.cuda.synchronize()
+    fused_ms = sum(ftimer.span(0, 1)) / steps
     res = dict(
         workload=label or w.name,
         step_ms=sum(step_ms) / steps,
         decode_ms=sum(dec_ms) / steps,
         decode_ms_p10_p90=[sorted(dec_ms)[steps // 10], sorted(dec_ms)[(9 * steps) // 10]],
         store_us=1000 * sum(store_ms) / steps,
+        fused_step_ms=fused_ms,
         bytes_logical=w.algorithmic_bytes(unique=False),
         bytes_unique=w.algorithmic_bytes(unique=True),
         flops=w.flops(),
@@ -193,6 +205,59 @@ def run_prefill(torch, binding, wl, w, steps, warmup, flush, scratch):
         store_GBps=w.store_bytes() / (store_ms * 1e-3) / 1e9,
     )
     res["mfma_frac"] = res["prefill_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
+    del t
+    return res
+
+
+def run_graph_small(torch, binding, wl, steps=200):
+    """Small decode batches are launch-bound: time back-to-back steps
+    (pa_store_kvcache + pa_decode) issued eagerly and as one HIP-graph replay
+    per step, wall clock over the whole run, no cache eviction."""
+    w = wl.custom_decode([512] * 8, block_size=256, num_q_heads=16, num_kv_heads=8, head_dim=128,
+                         dtype="bf16", seed=5, width=2)
+    t = wl.make_device_tensors(w)
+    slots = torch.from_numpy(w.slot_mapping).cuda()
+    tables = torch.from_numpy(w.block_tables).cuda()
+    ctx = torch.from_numpy(w.context_lens).cuda()
+    out = torch.empty_like(t["q"].contiguous())
+    need = binding.pa_decode_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                            w.block_size, w.max_blocks_per_seq, 0)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        binding.pa_store_kvcache(t["k"], t["v"], t["k_cache"], t["v_cache"], slots)
+        binding.pa_decode(t["q"], t["k_cache"], t["v_cache"], tables, ctx, w.scale, out=out,
+                          workspace=ws)
+
+    def fused():
+        binding.pa_store_decode(t["q"], t["k"], t["v"], slots, t["k_cache"], t["v_cache"], tables, ctx,
+                                w.scale, out=out, workspace=ws)
+
+    graphs = {}
+    for name, fn in (("graph", step), ("graph_fused", fused)):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graphs[name] = g
+    torch.cuda.synchronize()
+    res = {}
+    for name, fn in (("eager", step), ("eager_fused", fused), ("graph", graphs["graph"].replay),
+                     ("graph_fused", graphs["graph_fused"].replay)):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        res[f"{name}_us_per_step"] = round((time.perf_counter() - t0) / steps * 1e6, 2)
+    res["workload"] = "8 seqs x 512 tokens, qwen3-0.6b shapes, store + decode per step"
     del t
     return res
 
@@ -284,6 +349,9 @@ def main():
             torch.cuda.empty_cache()
             secondary[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
             log(f"[bench] {name}: decode {r['decode_ms']:.3f} ms, {r['decode_GBps_unique']:.0f} GB/s unique")
+        log("[bench] graph replay, small batch")
+        secondary["decode-graph-small"] = run_graph_small(torch, binding, wl)
+        log(f"[bench] small batch: {secondary['decode-graph-small']}")
         log("[bench] chunked-prefill")
         p = run_prefill(torch, binding, wl, wl.chunked_prefill(0), ks, 2, flush, scratch)
         torch.cuda.empty_cache()
@@ -340,6 +408,7 @@ def main():
             "decode_ms": round(head["decode_ms"], 5),
             "decode_ms_p10_p90": [round(x, 5) for x in head["decode_ms_p10_p90"]],
             "store_us": round(head["store_us"], 2),
+            "fused_store_decode_ms": round(head["fused_step_ms"], 5),
         },
         "secondary": secondary,
     }

@@ -238,18 +238,24 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
     return static_cast<uint64_t>((blk << log2_bs) + (pos & bs_mask)) * row_bytes;
   };
 
-  // the step's new row: local index in this partition (-1: not here / no store)
+  // The step's new row (fused scatter): local index in this partition, or -1
+  // when it is not here or not stored. Its head slice is copied to the cache
+  // slot once, here; the loops below read it from the inputs (so nothing in
+  // this launch reads the row it writes), selecting the address per row.
   int new_tl = -1;
   const char* nk_row = nullptr;
   const char* nv_row = nullptr;
-  int64_t new_dst = 0;
   if constexpr (FUSED) {
     const int slot = slot_mapping[b];
     if (slot >= 0 && n - 1 >= t0 && n - 1 < t1) {
       new_tl = n - 1 - t0;
       nk_row = new_k + static_cast<int64_t>(b) * new_k_stride_bytes + static_cast<int64_t>(g) * D * EB;
       nv_row = new_v + static_cast<int64_t>(b) * new_v_stride_bytes + static_cast<int64_t>(g) * D * EB;
-      new_dst = static_cast<int64_t>(slot) * static_cast<int64_t>(row_bytes) + static_cast<int64_t>(g) * D * EB;
+      const int64_t dst = static_cast<int64_t>(slot) * static_cast<int64_t>(row_bytes) +
+                          static_cast<int64_t>(g) * D * EB;
+      constexpr int kVecs = D * EB / 16;  // 16-byte vectors per head slice
+      if (tid < kVecs) store16(k_cache + dst + tid * 16, load16(nk_row + tid * 16));
+      else if (tid < 2 * kVecs) store16(v_cache + dst + (tid - kVecs) * 16, load16(nv_row + (tid - kVecs) * 16));
     }
   }
 
@@ -261,14 +267,9 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int tl = base + u * STEP1 + my_row1;
-      if (FUSED && tl == new_tl) {
-        // new row: from the inputs, and written to its cache slot
-        k0[u] = load16(nk_row + li1 * 16);
-        k1[u] = load16(nk_row + (LPT1 + li1) * 16);
-        store16(k_cache + new_dst + li1 * 16, k0[u]);
-        store16(k_cache + new_dst + (LPT1 + li1) * 16, k1[u]);
-      } else if (tl < ntok) {
+      if (tl < ntok) {
         const char* r = kbase1 + row_off(tl);
+        if constexpr (FUSED) r = tl == new_tl ? nk_row + li1 * 16 : r;
         k0[u] = load16_nt(r);
         k1[u] = load16_nt(r + LPT1 * 16);
       } else {
@@ -323,11 +324,12 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int tl = base + u * STEP + my_row;
-      if (FUSED && tl == new_tl) {
-        vv[u] = load16(nv_row + li * 16);
-        store16(v_cache + new_dst + li * 16, vv[u]);
+      if (tl < ntok) {
+        const char* r = vbase + row_off(tl);
+        if constexpr (FUSED) r = tl == new_tl ? nv_row + li * 16 : r;
+        vv[u] = load16_nt(r);
       } else {
-        vv[u] = tl < ntok ? load16_nt(vbase + row_off(tl)) : Vec16{{0u, 0u, 0u, 0u}};
+        vv[u] = Vec16{{0u, 0u, 0u, 0u}};
       }
     }
 #pragma unroll
@@ -502,10 +504,15 @@ hipError_t dispatch_fused(const DecodeArgs& a, hipStream_t stream) {
 int32_t decode_partition_tokens(int32_t requested, int32_t num_seqs, int32_t num_kv_heads,
                                 int32_t group, int32_t block_size, int32_t max_blocks) {
   if (requested > 0) return requested;
+  const int64_t max_ctx = static_cast<int64_t>(max_blocks) * block_size;
+  // Short histories: one pass, no merge launch (the launch latency of a
+  // second kernel costs more than the parallelism it would buy).
+  const int64_t one_pass = (max_ctx + 63) / 64 * 64;
+  if (one_pass <= 1024 && static_cast<int64_t>(group) * one_pass <= 8192)
+    return static_cast<int32_t>(one_pass);
   // Longest partition (fewest partials to merge) that still gives the grid
   // enough workgroups to cover the chip several times when every sequence
   // is as long as its table allows; the LDS score buffer caps group * length.
-  const int64_t max_ctx = static_cast<int64_t>(max_blocks) * block_size;
   const int64_t want = 8192;
   for (int32_t part : {1024, 512}) {
     if (static_cast<int64_t>(group) * part > 8192) continue;

@@ -6,6 +6,7 @@
 Operations:
   decode <workload>   pa_store_kvcache of the new tokens + pa_decode, inputs
                       resident, a 1 GiB read between calls (cold caches);
+  store_decode <workload>  the same step as one pa_store_decode launch;
   prefill             pa_store_kvcache + pa_prefill_varlen on chunked-prefill;
   copy                a 1 GiB device-to-device copy (counter calibration:
                       reads 1 GiB, writes 1 GiB).
@@ -24,7 +25,7 @@ if ROOT not in sys.path:
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("op", choices=["decode", "prefill", "copy"])
+    ap.add_argument("op", choices=["decode", "store_decode", "prefill", "copy"])
     ap.add_argument("workload", nargs="?", default="qwen3-0.6b-decode")
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--partition", type=int, default=0)
@@ -63,11 +64,15 @@ def main(argv=None):
         out = torch.empty_like(t["q"].contiguous())
         for _ in range(args.reps):
             scratch.amax()
+            if args.op == "store_decode":
+                binding.pa_store_decode(t["q"], t["k"], t["v"], slots, t["k_cache"], t["v_cache"], tables,
+                                        ctx, w.scale, out=out, partition_size=args.partition)
+                continue
             binding.pa_store_kvcache(t["k"], t["v"], t["k_cache"], t["v_cache"], slots)
             binding.pa_decode(t["q"], t["k_cache"], t["v_cache"], tables, ctx, w.scale, out=out,
                               partition_size=args.partition)
     torch.cuda.synchronize()
-    print(f"profile_ops {args.op} {args.workload if args.op == 'decode' else ''} done", flush=True)
+    print(f"profile_ops {args.op} {args.workload if 'decode' in args.op else ''} done", flush=True)
 
 
 if __name__ == "__main__":
