@@ -3,6 +3,7 @@
 Only the tests, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
 leg may use this package; the library never imports it.
 """
+from . import fp8  # noqa: F401
 from .paged_attention import (  # noqa: F401
     decode,
     gather_history,
@@ -10,4 +11,5 @@ from .paged_attention import (  # noqa: F401
     softmax_attention,
     store_kvcache,
     widen,
+    widen_kv,
 )

@@ -15,6 +15,9 @@ softmax(scale * q K^T) V in fp64.
 
 Storage formats: fp32 tensors are numpy float32; bf16 tensors are numpy
 uint16 arrays holding the bf16 bit patterns, widened exactly to fp64 here.
+An fp8 cache ("fp8e4m3") is a numpy uint8 array of E4M3 codes with one scale
+per tensor; its rows widen to value(code) * scale (``oracle.fp8``), and the
+queries and outputs keep the 16-bit type.
 
 Readings of points the pages leave open (each is also listed in the design
 notes of the repository):
@@ -36,6 +39,8 @@ notes of the repository):
 from __future__ import annotations
 
 import numpy as np
+
+from . import fp8
 
 
 def widen(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -70,16 +75,25 @@ def store_kvcache(key, value, k_cache, v_cache, slot_mapping) -> None:
         v_cache[block, offset] = value[t]
 
 
-def gather_history(cache, table_row, n: int, kv_head: int, dtype: str) -> np.ndarray:
+def widen_kv(x: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
+    """Exact fp64 values of stored cache elements: ``widen`` for fp32 / bf16,
+    value(code) * scale for an fp8 cache."""
+    if dtype == "fp8e4m3":
+        return fp8.dequantize(x, scale)
+    return widen(x, dtype)
+
+
+def gather_history(cache, table_row, n: int, kv_head: int, dtype: str, scale: float = 1.0) -> np.ndarray:
     """Copy the first ``n`` logical rows of one kv head of one sequence into a
     contiguous fp64 [n, D] buffer by walking its block table ("nano-vLLM
     Part 2 ...", section 2.2: logical page p // bs lives in physical block
-    table[p // bs] at offset p % bs)."""
+    table[p // bs] at offset p % bs). ``scale`` is the per-tensor scale of an
+    fp8 cache."""
     block_size = cache.shape[1]
     n_pages = -(-n // block_size)
     pages = [cache[int(table_row[j]), :, kv_head, :] for j in range(n_pages)]
     rows = np.concatenate(pages, axis=0)[:n] if pages else cache[:0, :, kv_head, :].reshape(0, cache.shape[-1])
-    return widen(rows, dtype)
+    return widen_kv(rows, dtype, scale)
 
 
 def softmax_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
@@ -91,7 +105,7 @@ def softmax_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float)
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, dtype: str,
-           seqs=None) -> np.ndarray:
+           seqs=None, kv_dtype=None, k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """Paged decode attention: one query per sequence over its whole cached
     history ("Inference Engine Inside nano-vLLM", "Attention in nano-vLLM",
     the flash_attn_with_kvcache branch; "From nano-vLLM to vLLM ...",
@@ -100,7 +114,8 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, dtype:
     q: [B, H_q, D] storage dtype; caches [N, bs, H_kv, D]; block_tables int
     [B, W]; context_lens int [B]. Returns fp64 [B, H_q, D]. With ``seqs`` (a
     list of sequence indices) only those rows are computed; the others are
-    NaN.
+    NaN. ``kv_dtype`` (default: ``dtype``) is the caches' storage type; for
+    "fp8e4m3" the caches hold codes scaled by ``k_scale`` / ``v_scale``.
     """
     B, H_q, D = q.shape
     H_kv = k_cache.shape[2]
@@ -113,15 +128,16 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, dtype:
             continue
         qb = widen(q[b], dtype)
         for g in range(H_kv):
-            K = gather_history(k_cache, block_tables[b], n, g, dtype)
-            V = gather_history(v_cache, block_tables[b], n, g, dtype)
+            K = gather_history(k_cache, block_tables[b], n, g, kv_dtype or dtype, k_scale)
+            V = gather_history(v_cache, block_tables[b], n, g, kv_dtype or dtype, v_scale)
             for h in range(g * G, (g + 1) * G):  # query heads of kv head g: h // G == g
                 out[b, h] = softmax_attention(qb[h], K, V, scale)
     return out
 
 
 def prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_tables, scale: float,
-                   dtype: str, rows=None, k=None, v=None) -> np.ndarray:
+                   dtype: str, rows=None, k=None, v=None, kv_dtype=None, k_scale: float = 1.0,
+                   v_scale: float = 1.0) -> np.ndarray:
     """Packed variable-length causal prefill ("Inference Engine Inside
     nano-vLLM", "Attention in nano-vLLM", the flash_attn_varlen_func branch;
     "nano-vLLM Part 2 ...", sections 2.5 and 4.1).
@@ -135,6 +151,8 @@ def prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_tables
 
     q: [Tq, H_q, D]. Returns fp64 [Tq, H_q, D]; with ``rows`` (global query
     row indices) only those rows are computed and the others are NaN.
+    ``kv_dtype`` / ``k_scale`` / ``v_scale`` describe a paged fp8 cache as in
+    ``decode``.
     """
     Tq, H_q, D = q.shape
     H_kv = (k_cache if block_tables is not None else k).shape[-2]
@@ -152,8 +170,8 @@ def prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_tables
             continue
         for g in range(H_kv):
             if block_tables is not None:
-                K = gather_history(k_cache, block_tables[i], Lk, g, dtype)
-                V = gather_history(v_cache, block_tables[i], Lk, g, dtype)
+                K = gather_history(k_cache, block_tables[i], Lk, g, kv_dtype or dtype, k_scale)
+                V = gather_history(v_cache, block_tables[i], Lk, g, kv_dtype or dtype, v_scale)
             else:
                 k0 = int(cu_seqlens_k[i])
                 K = widen(k[k0:k0 + Lk, g, :], dtype)

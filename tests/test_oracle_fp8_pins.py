@@ -1,0 +1,241 @@
+"""Pins of the fp8 (E4M3) cache oracle to things other than itself.
+
+* library routine: torch's float8_e4m3fn type (its own implementation of the
+  OCP format) gives the value of every one of the 256 codes, and its
+  float32 -> float8_e4m3fn cast (round to nearest even) gives the code of
+  every value below the saturation threshold, ties included; torch's fp32
+  division gives the quotient the quantiser must round;
+* closed forms worked by hand from the field definition (1.0, the largest
+  value, the subnormal ladder, half-way cases, saturation, NaN, signed zero);
+* invariants: every finite code survives encode(decode(c)); encoding is
+  monotone; an fp8 cache with unit scales attends exactly like a bf16 cache
+  holding the same values (every E4M3 value is a bf16 value); k_scale acts as
+  a factor on the softmax scale and v_scale as a factor on the output.
+
+The last test plants plausible mistakes in copies of ``oracle/fp8.py`` and
+checks that every mutant fails at least one pin.
+"""
+from __future__ import annotations
+
+import inspect
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.fp8 as fp8_src
+from paged_kv_cache_66_amd import workloads as wl
+
+
+def _torch_values():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _torch_encode(y32: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(y32, dtype=np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+# --------------------------------------------------------------------------
+# pin batteries, each taking an fp8 namespace (real or mutant)
+# --------------------------------------------------------------------------
+
+
+def pin_value_table(f):
+    ref = _torch_values()
+    got = np.array([f.e4m3_value(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert list(np.nonzero(nan)[0]) == [0x7F, 0xFF]
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def pin_encode_vs_torch(f):
+    vals = _torch_values()
+    fin = np.sort(np.unique(vals[np.isfinite(vals) & (vals >= 0)]))
+    mids = (fin[:-1] + fin[1:]) / 2          # exact half-way points (fp32-representable)
+    rng = np.random.default_rng(0)
+    y = np.concatenate([
+        fin, mids, -mids, np.nextafter(mids.astype(np.float32), np.float32(np.inf)),
+        np.nextafter(mids.astype(np.float32), np.float32(-np.inf)),
+        rng.standard_normal(3000) * 8, rng.standard_normal(500) * 0.01,
+        rng.uniform(-447.9, 447.9, 500),
+    ]).astype(np.float32)
+    y = y[np.abs(y) < 448]
+    assert np.array_equal(f.encode(y.astype(np.float64)), _torch_encode(y))
+
+
+def pin_closed_forms(f):
+    cases = [  # (value, code); a list, since 0.0 and -0.0 are equal dict keys
+        (1.0, 0x38),            # exponent 7 (bias 7), mantissa 0
+        (2.0, 0x40),
+        (-1.5, 0xBC),           # sign, exponent 7, mantissa 4
+        (448.0, 0x7E),          # 1.75 * 2^8, the largest finite value
+        (2.0 ** -6, 0x08),      # smallest normal
+        (2.0 ** -9, 0x01),      # smallest subnormal: 1/8 * 2^-6
+        (7 * 2.0 ** -9, 0x07),  # largest subnormal
+        (2.0 ** -10, 0x00),     # half of the smallest subnormal: tie, even code 0 wins
+        (3 * 2.0 ** -10, 0x02), # tie between 1 and 2 subnormal steps: even (2) wins
+        (1.0625, 0x38),         # tie between 1.0 and 1.125: even mantissa 0
+        (1.1875, 0x3A),         # tie between 1.125 and 1.25: even mantissa 2
+        (0.10009765625, 0x1D),  # bf16(0.1): between 0.09375 (0x1C) and 0.1015625 (0x1D), nearer the latter
+        (464.0, 0x7E),          # saturates
+        (1e30, 0x7E),
+        (np.inf, 0x7E),
+        (-np.inf, 0xFE),
+        (-500.0, 0xFE),
+        (0.0, 0x00),
+        (-0.0, 0x80),
+    ]
+    for y, code in cases:
+        assert f.encode_one(y) == code, (y, hex(code))
+    assert f.encode_one(np.nan) == 0x7F
+    assert f.encode_one(-np.nan) == 0xFF
+
+
+def pin_round_trip_and_order(f):
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    assert np.array_equal(f.encode(f.decode(codes)), codes)
+    ys = np.linspace(-460.0, 460.0, 4001)
+    v = f.decode(f.encode(ys))
+    assert np.all(np.diff(v) >= 0)
+    assert np.max(np.abs(v - np.clip(ys, -448, 448)) / np.maximum(np.abs(ys), 2.0 ** -6)) <= 2.0 ** -4 + 1e-12
+
+
+def pin_quantize_fp32_quotient(f):
+    """The code is decided on the fp32 quotient (torch's fp32 division then
+    torch's cast), including inputs whose fp32 quotient lands exactly on a
+    half-way point while the exact quotient does not."""
+    rng = np.random.default_rng(1)
+    x = wl.f32_to_bf16_bits(rng.standard_normal(4000).astype(np.float32) * 3)
+    x64 = oracle.widen(x, "bf16")
+    for scale in (0.013, 0.3, 1.0, 1.7, 3.0):
+        y32 = (torch.from_numpy(x64.astype(np.float32)) / torch.tensor(scale, dtype=torch.float32)).numpy()
+        keep = np.abs(y32) < 448
+        assert np.array_equal(f.quantize(x64, scale)[keep], _torch_encode(y32[keep]))
+        assert np.all(f.quantize(x64, scale)[~keep] & 0x7F == 0x7E)
+    # scales just above 1 and inputs x = fp32(1.0625 * scale) whose exact
+    # quotient lies above the half-way point 1.0625 while the fp32 quotient is
+    # exactly on it: the fp32 tie goes to the even mantissa (1.0, code 0x38),
+    # where the exact quotient would round up to 1.125 (0x39)
+    mid = 1.0625
+    cases = []
+    for k in range(1, 20000):
+        scale = np.float32(1.0 + k * 2.0 ** -23)
+        x32 = np.float32(mid * float(scale))
+        q32 = (torch.tensor(float(x32), dtype=torch.float32) / torch.tensor(float(scale), dtype=torch.float32)).item()
+        if q32 == mid and float(x32) / float(scale) > mid:
+            cases.append((float(x32), float(scale)))
+    assert cases, "no fp32-tie case found"
+    for x, scale in cases[:20]:
+        assert f.quantize(np.array([x]), scale)[0] == 0x38, (x, scale)
+
+
+def pin_store_rows(f):
+    kc = np.full((3, 4, 1, 4), 0x55, dtype=np.uint8)
+    vc = kc.copy()
+    key = np.array([[[1.0, -2.0, 448.0, 2.0 ** -10]], [[0.5, 0.25, 3.0, -0.0]],
+                    [[2.0 ** -9, -1.0, 0.0, 1.0625]]])
+    val = -key
+    f.store_kvcache(key, val, kc, vc, np.array([5, -1, 0]), 1.0, 2.0)
+    assert list(kc[1, 1, 0]) == [0x38, 0xC0, 0x7E, 0x00]
+    assert list(kc[0, 0, 0]) == [0x01, 0xB8, 0x00, 0x38]   # slot 0 is a real slot
+    # -x / 2 = -0.5, 1.0, -224 (1.75 * 2^7: exponent 14, mantissa 6), -2^-11 (rounds to -0)
+    assert list(vc[1, 1, 0]) == [0xB0, 0x38, 0xF6, 0x80]
+    untouched = np.ones(kc.shape, bool)
+    untouched[1, 1] = False
+    untouched[0, 0] = False
+    assert np.all(kc[untouched] == 0x55) and np.all(vc[untouched] == 0x55)
+
+
+def pin_attention_with_fp8_cache(f):
+    """fp8 attention through the oracle entry points: unit scales equal a bf16
+    cache with the same values; k_scale multiplies the softmax scale; v_scale
+    multiplies the output."""
+    rng = np.random.default_rng(2)
+    N, bs, hkv, d, hq = 6, 4, 2, 8, 4
+    codes_k = rng.integers(0, 256, size=(N, bs, hkv, d), dtype=np.uint8)
+    codes_v = rng.integers(0, 256, size=(N, bs, hkv, d), dtype=np.uint8)
+    for c in (codes_k, codes_v):
+        c[(c & 0x7F) == 0x7F] = 0x30  # no NaN codes in attended rows
+    codes_k &= 0xBF  # keep |k| <= 2^0 * 1.875 range small: exponent bit 6 cleared
+    tv = _torch_values()  # every finite E4M3 value is a bf16 value
+    kv_bf16_k = wl.f32_to_bf16_bits(tv[codes_k].astype(np.float32))
+    kv_bf16_v = wl.f32_to_bf16_bits(tv[codes_v].astype(np.float32))
+    q = wl.f32_to_bf16_bits(rng.standard_normal((2, hq, d)).astype(np.float32))
+    tables = np.array([[3, 0, 5], [1, 4, -1]], dtype=np.int32)
+    ctx = np.array([11, 6], dtype=np.int32)
+    ref = oracle.decode(q, kv_bf16_k, kv_bf16_v, tables, ctx, 0.3, "bf16")
+    got = oracle.decode(q, codes_k, codes_v, tables, ctx, 0.3, "bf16", kv_dtype="fp8e4m3")
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    got_k = oracle.decode(q, codes_k, codes_v, tables, ctx, 0.3, "bf16", kv_dtype="fp8e4m3", k_scale=2.0)
+    ref_k = oracle.decode(q, kv_bf16_k, kv_bf16_v, tables, ctx, 0.6, "bf16")
+    np.testing.assert_allclose(got_k, ref_k, rtol=1e-12, atol=1e-12)
+    got_v = oracle.decode(q, codes_k, codes_v, tables, ctx, 0.3, "bf16", kv_dtype="fp8e4m3", v_scale=0.25)
+    np.testing.assert_allclose(got_v, ref * 0.25, rtol=1e-12, atol=1e-12)
+    cuq = np.array([0, 3, 5], dtype=np.int32)
+    cuk = np.array([0, 11, 17], dtype=np.int32)
+    qp = wl.f32_to_bf16_bits(rng.standard_normal((5, hq, d)).astype(np.float32))
+    ref_p = oracle.prefill_varlen(qp, kv_bf16_k, kv_bf16_v, cuq, cuk, tables, 0.3, "bf16")
+    got_p = oracle.prefill_varlen(qp, codes_k, codes_v, cuq, cuk, tables, 0.3, "bf16",
+                                  kv_dtype="fp8e4m3", k_scale=1.0, v_scale=3.0)
+    np.testing.assert_allclose(got_p, ref_p * 3.0, rtol=1e-12, atol=1e-12)
+
+
+PINS = [pin_value_table, pin_encode_vs_torch, pin_closed_forms, pin_round_trip_and_order,
+        pin_quantize_fp32_quotient, pin_store_rows, pin_attention_with_fp8_cache]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_fp8_oracle_pin(pin):
+    pin(oracle.fp8)
+
+
+# --------------------------------------------------------------------------
+# mutation check
+# --------------------------------------------------------------------------
+
+MUTANTS = [
+    ("exponent bias 8", "2.0 ** (exp - 7)", "2.0 ** (exp - 8)"),
+    ("subnormals without the 2^-6 factor", "(man / 8.0) * 2.0 ** -6", "(man / 8.0) * 2.0 ** -7"),
+    ("subnormals with an implicit one", "return sign * (man / 8.0) * 2.0 ** -6",
+     "return sign * (1.0 + man / 8.0) * 2.0 ** -6"),
+    ("ties away from zero", "code = int([c for c in cands if c % 2 == 0][0])", "code = int(max(cands))"),
+    ("ties toward zero", "code = int([c for c in cands if c % 2 == 0][0])", "code = int(min(cands))"),
+    ("no saturation", "if a >= 448.0:\n        code = 0x7E", "if a > 1e300:\n        code = 0x7E"),
+    ("NaN loses its sign", "return 0xFF if neg else 0x7F", "return 0x7F"),
+    ("fp64 quotient", "y = np.asarray(x64, dtype=np.float64).astype(np.float32) / np.float32(scale)",
+     "y = np.asarray(x64, dtype=np.float64) / float(np.float32(scale))"),
+    ("scale multiplies on store", "/ np.float32(scale)\n", "* np.float32(scale)\n"),
+    ("dequantize ignores scale", "return decode(codes) * float(np.float32(scale))", "return decode(codes)"),
+    ("store skips slot 0", "if s < 0:", "if s <= 0:"),
+    ("V stored with the K scale", "v_cache[block, offset] = quantize(value64[t], v_scale)",
+     "v_cache[block, offset] = quantize(value64[t], k_scale)"),
+]
+
+
+def _mutant(old, new):
+    src = inspect.getsource(fp8_src)
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    ns: dict = {"__name__": "oracle.fp8_mutant", "__package__": "oracle"}
+    exec(compile(src.replace(old, new), "oracle_fp8_mutant", "exec"), ns)
+    return types.SimpleNamespace(**ns)
+
+
+@pytest.mark.parametrize("desc,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_fp8_pins_catch_planted_mistake(desc, old, new, monkeypatch):
+    mut = _mutant(old, new)
+    # the attention pin reaches the fp8 code through oracle.paged_attention
+    monkeypatch.setattr(oracle.paged_attention, "fp8", mut)
+    caught = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mut)
+        except Exception:  # assertion or a crash both count as caught
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught mutant: {desc}"

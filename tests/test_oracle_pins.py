@@ -410,8 +410,8 @@ MUTANTS = [
     ("top-left causal alignment", "visible = start + j + 1", "visible = j + 1"),
     ("table ignored", "pages = [cache[int(table_row[j]), :, kv_head, :] for j in range(n_pages)]",
      "pages = [cache[j, :, kv_head, :] for j in range(n_pages)]"),
-    ("K and V swapped", "K = gather_history(k_cache, block_tables[b], n, g, dtype)",
-     "K = gather_history(v_cache, block_tables[b], n, g, dtype)"),
+    ("K and V swapped", "K = gather_history(k_cache, block_tables[b], n, g, kv_dtype or dtype, k_scale)",
+     "K = gather_history(v_cache, block_tables[b], n, g, kv_dtype or dtype, k_scale)"),
     ("new token excluded", "n = int(context_lens[b])", "n = int(context_lens[b]) - 1"),
     ("store block/offset swapped", "block, offset = divmod(s, block_size)",
      "offset, block = divmod(s, block_size)"),
@@ -424,7 +424,7 @@ MUTANTS = [
 def _mutant(old, new):
     src = inspect.getsource(oracle_src)
     assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
-    ns: dict = {"__name__": "oracle_mutant"}
+    ns: dict = {"__name__": "oracle.mutant", "__package__": "oracle"}
     exec(compile(src.replace(old, new), "oracle_mutant", "exec"), ns)
     return types.SimpleNamespace(**ns)
 
