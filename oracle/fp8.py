@@ -17,12 +17,13 @@ listed in the design notes of the repository):
 * scaling: one fp32 scale per cache tensor (k_scale for K, v_scale for V).
   A stored code c stands for value(c) * scale.
 * quantising a value x (held in the input's storage type) for the cache:
-  y = fp32(x) / fp32(scale), the fp32 quotient rounded to nearest; then the
+  y = fp32(|x|) / fp32(scale), the fp32 quotient rounded to nearest; then the
   finite E4M3 value nearest to y, ties to the code with an even mantissa;
-  magnitudes beyond 448 (infinities included) saturate to +-448; NaN stays
-  NaN and keeps its sign bit. The quotient is taken in fp32 because that is
-  the precision the device takes it in, and the code is an integer decided
-  by it.
+  magnitudes of 448 and beyond (infinities included) saturate to 448; a NaN
+  gives the NaN code. The code's sign bit is x's sign bit (so -0 and a
+  negative NaN keep it; the sign of a NaN quotient is left to no hardware).
+  The quotient is taken in fp32 because that is the precision the device
+  takes it in, and the code is an integer decided by it.
 """
 from __future__ import annotations
 
@@ -76,17 +77,33 @@ def encode_one(y: float) -> int:
 
 
 def encode(y) -> np.ndarray:
-    """Elementwise ``encode_one`` over an array; returns uint8 codes."""
-    y = np.asarray(y)
-    return np.array([encode_one(v) for v in y.ravel()], dtype=np.uint8).reshape(y.shape)
+    """``encode_one`` over an array, as a sorted search: the two finite
+    values that bracket |y| are found with ``np.searchsorted`` over the
+    increasing non-negative values, the nearer one wins and a tie goes to
+    the even code (neighbouring codes alternate parity). Returns uint8."""
+    y = np.asarray(y, dtype=np.float64)
+    neg = np.signbit(y)
+    nan = np.isnan(y)
+    a = np.where(nan, 0.0, np.minimum(np.abs(y), 448.0))   # 448 and beyond saturate
+    hi = np.clip(np.searchsorted(_POS_VALUES, a, side="left"), 0, 0x7E)  # first value >= a
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_lo = a - _POS_VALUES[lo]
+    d_hi = _POS_VALUES[hi] - a
+    code = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(nan, 0x7F, code)
+    return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
 
 
 def quantize(x64: np.ndarray, scale: float) -> np.ndarray:
     """Codes for exact input values ``x64`` (already widened from their
     storage type, so exactly representable in fp32) under a per-tensor
-    scale: y = fp32(x) / fp32(scale) in fp32, then ``encode``."""
-    y = np.asarray(x64, dtype=np.float64).astype(np.float32) / np.float32(scale)
-    return encode(y.astype(np.float64))
+    scale: the magnitude code of y = fp32(|x|) / fp32(scale) taken in fp32,
+    with x's sign bit."""
+    with np.errstate(over="ignore", invalid="ignore"):  # inf / NaN inputs are part of the domain
+        x32 = np.asarray(x64, dtype=np.float64).astype(np.float32)
+        y = np.abs(x32) / np.float32(scale)
+    mag = encode(y.astype(np.float64)) & 0x7F
+    return (mag | np.where(np.signbit(x32), 0x80, 0)).astype(np.uint8)
 
 
 def dequantize(codes, scale: float) -> np.ndarray:

@@ -69,6 +69,19 @@ def pin_encode_vs_torch(f):
     assert np.array_equal(f.encode(y.astype(np.float64)), _torch_encode(y))
 
 
+def pin_vector_encode_matches_scalar(f):
+    """The sorted-search encoder and the brute-force scalar one agree on
+    values, half-way points, their fp32 neighbours, NaN and +-inf."""
+    vals = np.array([f.e4m3_value(c) for c in range(0x7F)])
+    mids = (vals[:-1] + vals[1:]) / 2
+    m32 = mids.astype(np.float32)
+    y = np.concatenate([vals, mids, -mids, np.nextafter(m32, np.float32(1e9)).astype(np.float64),
+                        np.nextafter(m32, np.float32(-1e9)).astype(np.float64),
+                        np.random.default_rng(3).standard_normal(2000) * 50,
+                        [np.nan, -np.nan, np.inf, -np.inf, 448.0, 447.9, 464.0, 1e9, 0.0, -0.0]])
+    assert np.array_equal(f.encode(y), np.array([f.encode_one(v) for v in y], dtype=np.uint8))
+
+
 def pin_closed_forms(f):
     cases = [  # (value, code); a list, since 0.0 and -0.0 are equal dict keys
         (1.0, 0x38),            # exponent 7 (bias 7), mantissa 0
@@ -135,6 +148,15 @@ def pin_quantize_fp32_quotient(f):
         assert f.quantize(np.array([x]), scale)[0] == 0x38, (x, scale)
 
 
+def pin_quantize_specials(f):
+    """Sign and NaN handling of the store: the code carries x's sign bit, NaN
+    inputs give the NaN code, infinities and large values saturate."""
+    x = np.array([np.nan, -np.nan, np.inf, -np.inf, 0.0, -0.0, 1e6, -1e6, -3.0])
+    got = f.quantize(x, 0.5)
+    # -3 / 0.5 = -6 = -1.5 * 2^2: sign, exponent 9, mantissa 4 -> 0xCC
+    assert list(got) == [0x7F, 0xFF, 0x7E, 0xFE, 0x00, 0x80, 0x7E, 0xFE, 0xCC]
+
+
 def pin_store_rows(f):
     kc = np.full((3, 4, 1, 4), 0x55, dtype=np.uint8)
     vc = kc.copy()
@@ -186,8 +208,8 @@ def pin_attention_with_fp8_cache(f):
     np.testing.assert_allclose(got_p, ref_p * 3.0, rtol=1e-12, atol=1e-12)
 
 
-PINS = [pin_value_table, pin_encode_vs_torch, pin_closed_forms, pin_round_trip_and_order,
-        pin_quantize_fp32_quotient, pin_store_rows, pin_attention_with_fp8_cache]
+PINS = [pin_value_table, pin_encode_vs_torch, pin_vector_encode_matches_scalar, pin_closed_forms, pin_round_trip_and_order,
+        pin_quantize_fp32_quotient, pin_quantize_specials, pin_store_rows, pin_attention_with_fp8_cache]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -204,13 +226,21 @@ MUTANTS = [
     ("subnormals without the 2^-6 factor", "(man / 8.0) * 2.0 ** -6", "(man / 8.0) * 2.0 ** -7"),
     ("subnormals with an implicit one", "return sign * (man / 8.0) * 2.0 ** -6",
      "return sign * (1.0 + man / 8.0) * 2.0 ** -6"),
-    ("ties away from zero", "code = int([c for c in cands if c % 2 == 0][0])", "code = int(max(cands))"),
-    ("ties toward zero", "code = int([c for c in cands if c % 2 == 0][0])", "code = int(min(cands))"),
-    ("no saturation", "if a >= 448.0:\n        code = 0x7E", "if a > 1e300:\n        code = 0x7E"),
-    ("NaN loses its sign", "return 0xFF if neg else 0x7F", "return 0x7F"),
-    ("fp64 quotient", "y = np.asarray(x64, dtype=np.float64).astype(np.float32) / np.float32(scale)",
-     "y = np.asarray(x64, dtype=np.float64) / float(np.float32(scale))"),
-    ("scale multiplies on store", "/ np.float32(scale)\n", "* np.float32(scale)\n"),
+    ("scalar ties away from zero", "code = int([c for c in cands if c % 2 == 0][0])", "code = int(max(cands))"),
+    ("scalar ties toward zero", "code = int([c for c in cands if c % 2 == 0][0])", "code = int(min(cands))"),
+    ("scalar no saturation", "if a >= 448.0:\n        code = 0x7E", "if a > 1e300:\n        code = 0x7E"),
+    ("scalar NaN loses its sign", "return 0xFF if neg else 0x7F", "return 0x7F"),
+    ("vector ties away from zero", "np.where(lo % 2 == 0, lo, hi)", "hi"),
+    ("vector ties toward zero", "np.where(lo % 2 == 0, lo, hi)", "lo"),
+    ("vector ties to odd", "np.where(lo % 2 == 0, lo, hi)", "np.where(lo % 2 == 1, lo, hi)"),
+    ("vector always rounds down", "code = np.where(d_lo < d_hi, lo,", "code = np.where(d_lo <= d_hi + 1e9, lo,"),
+    ("vector bracket off by one", "lo = np.clip(hi - 1, 0, 0x7E)", "lo = np.clip(hi - 2, 0, 0x7E)"),
+    ("vector NaN is zero", "code = np.where(nan, 0x7F, code)", "code = code"),
+    ("fp64 quotient", "        y = np.abs(x32) / np.float32(scale)",
+     "        y = np.abs(np.asarray(x64, dtype=np.float64)) / float(np.float32(scale))"),
+    ("scale multiplies on store", "        y = np.abs(x32) / np.float32(scale)", "        y = np.abs(x32) * np.float32(scale)"),
+    ("store drops the sign", "return (mag | np.where(np.signbit(x32), 0x80, 0)).astype(np.uint8)",
+     "return mag.astype(np.uint8)"),
     ("dequantize ignores scale", "return decode(codes) * float(np.float32(scale))", "return decode(codes)"),
     ("store skips slot 0", "if s < 0:", "if s <= 0:"),
     ("V stored with the K scale", "v_cache[block, offset] = quantize(value64[t], v_scale)",
