@@ -36,7 +36,9 @@
  *   done in 64 bits.
  * Dtypes.  One element type for q, keys, values, caches and outputs:
  *   PA_F32 or PA_BF16. Accumulation is always fp32; bf16 outputs are rounded
- *   to nearest even once at the end.
+ *   to nearest even once at the end. The *_fp8 entry points (end of this
+ *   file) keep one-byte E4M3 caches instead, next to bf16 q / key / value /
+ *   outputs.
  * Errors.  Every problem the host can see (null pointer, bad size,
  *   unsupported head_dim / block_size / dtype, misalignment, too-small
  *   workspace) returns a non-zero pa_status and enqueues nothing. A failed
@@ -234,6 +236,77 @@ pa_status pa_prefill_varlen(void* out, const void* q, int64_t q_row_stride, int3
                             int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                             int32_t num_blocks, float scale, pa_dtype dtype, void* stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * fp8 KV caches
+ * ---------------------------------------------------------------------------
+ * The pages size a cache element by its data type and count fp8 at one byte
+ * per element ("nano-vLLM Part 2: Block Tables, KV Cache, and the Path to
+ * the GPU", section 1, the KV-cache shape and its dtype factor); they give no
+ * format, so the one built here is:
+ *   element  OCP 8-bit float E4M3 ("E4M3FN"): sign, 4 exponent bits (bias 7),
+ *            3 mantissa bits, subnormals, no infinities, 0x7F / 0xFF = NaN,
+ *            largest magnitude 448;
+ *   scaling  one fp32 scale per tensor: k_scale for the K cache, v_scale for
+ *            the V cache; code c stands for value(c) * scale;
+ *   storing  x (bf16) -> y = fp32(x) / scale (fp32 division, correctly
+ *            rounded) -> nearest E4M3 value, ties to even mantissa,
+ *            |y| >= 448 (and +-inf) saturate to +-448, NaN stays NaN.
+ * Caches are [num_blocks, block_size, num_kv_heads, head_dim] bytes, laid out
+ * exactly as the 16-bit caches, 16-byte aligned. q, key, value and out are
+ * bf16 (dtype must be PA_BF16). Scales must be finite and > 0
+ * (PA_ERR_SHAPE otherwise). Everything else — ownership, index arrays,
+ * errors, preconditions, workspace sizing, partitioning, causality — is as
+ * for the entry point without the suffix.
+ */
+
+/* pa_store_kvcache with quantisation: cache row slot receives the E4M3 codes
+ * of key[t] / k_scale and value[t] / v_scale. */
+pa_status pa_store_kvcache_fp8(const void* key, int64_t key_row_stride,
+                               const void* value, int64_t value_row_stride,
+                               void* k_cache, void* v_cache,
+                               const int32_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_blocks, int32_t block_size,
+                               int32_t num_kv_heads, int32_t head_dim,
+                               float k_scale, float v_scale, pa_dtype dtype, void* stream);
+
+/* pa_decode over fp8 caches: keys are value(code) * k_scale, values
+ * value(code) * v_scale. */
+pa_status pa_decode_fp8(void* out, const void* q, int64_t q_row_stride,
+                        const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, int32_t num_seqs,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int32_t num_blocks, float scale,
+                        float k_scale, float v_scale, int32_t partition_size,
+                        pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* pa_store_decode over fp8 caches: bit for bit pa_store_kvcache_fp8 then
+ * pa_decode_fp8 with the same arguments (same slot_mapping precondition as
+ * pa_store_decode). */
+pa_status pa_store_decode_fp8(void* out, const void* q, int64_t q_row_stride, const void* key,
+                              int64_t key_row_stride, const void* value, int64_t value_row_stride,
+                              const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, float scale, float k_scale, float v_scale,
+                              int32_t partition_size, pa_dtype dtype, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* pa_prefill_varlen over fp8 paged caches (block_tables must not be NULL:
+ * the packed mode reads this step's bf16 k / v and is pa_prefill_varlen's). */
+pa_status pa_prefill_varlen_fp8(void* out, const void* q, int64_t q_row_stride, int32_t total_q,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                float scale, float k_scale, float v_scale, pa_dtype dtype,
+                                void* stream);
 
 #ifdef __cplusplus
 }

@@ -45,6 +45,16 @@ _SIGNATURES = {
     "pa_prefill_varlen": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _i64, _vp, _i64, _vp, _vp, _i32,
                                          _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                          _f32, ctypes.c_int, _vp]),
+    "pa_store_kvcache_fp8": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                            _i32, _f32, _f32, ctypes.c_int, _vp]),
+    "pa_decode_fp8": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                     _i32, _i32, _f32, _f32, _f32, _i32, ctypes.c_int, _vp, _sz, _vp]),
+    "pa_store_decode_fp8": (ctypes.c_int, [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp,
+                                           _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32,
+                                           _f32, _i32, ctypes.c_int, _vp, _sz, _vp]),
+    "pa_prefill_varlen_fp8": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
+                                             _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32,
+                                             _f32, ctypes.c_int, _vp]),
 }
 
 
@@ -118,6 +128,23 @@ def _cache_dims(k_cache, v_cache):
     return tuple(int(x) for x in k_cache.shape)
 
 
+def _fp8_cache_dims(k_cache, v_cache):
+    """Dims of E4M3 caches held as uint8 (or torch.float8_e4m3fn) tensors."""
+    import torch
+    _require(k_cache.dtype in (torch.uint8, torch.float8_e4m3fn), "fp8 caches must be uint8 / float8_e4m3fn")
+    return _cache_dims(k_cache, v_cache)
+
+
+def _workspace(workspace, b, hq, hkv, d, bs, w, partition_size, device):
+    import torch
+    need = pa_decode_workspace_size(b, hq, hkv, d, bs, w, partition_size) if b > 0 else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    wp = workspace.data_ptr() if workspace is not None else None
+    wn = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return wp, wn
+
+
 def pa_store_kvcache(key, value, k_cache, v_cache, slot_mapping) -> None:
     """Scatter key/value rows [T, H_kv, D] into the caches at slot_mapping."""
     lib = load()
@@ -158,11 +185,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None, 
     if out is None:
         out = torch.empty((b, hq, d), dtype=q.dtype, device=q.device)
     _require(out.is_contiguous() and tuple(out.shape) == (b, hq, d) and out.dtype == q.dtype, "out")
-    need = pa_decode_workspace_size(b, hq, hkv, d, bs, w, partition_size) if b > 0 else 0
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    wp = workspace.data_ptr() if workspace is not None else None
-    wn = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    wp, wn = _workspace(workspace, b, hq, hkv, d, bs, w, partition_size, q.device)
     st = lib.pa_decode(out.data_ptr(), qp, qs, k_cache.data_ptr(), v_cache.data_ptr(),
                        block_tables.data_ptr(), w, context_lens.data_ptr(), b, hq, hkv, d, bs, n,
                        float(scale), int(partition_size), _dtype_code(q), wp, wn, _stream(q))
@@ -195,11 +218,7 @@ def pa_store_decode(q, key, value, slot_mapping, k_cache, v_cache, block_tables,
     if out is None:
         out = torch.empty((b, hq, d), dtype=q.dtype, device=q.device)
     _require(out.is_contiguous() and tuple(out.shape) == (b, hq, d) and out.dtype == q.dtype, "out")
-    need = pa_decode_workspace_size(b, hq, hkv, d, bs, w, partition_size) if b > 0 else 0
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    wp = workspace.data_ptr() if workspace is not None else None
-    wn = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    wp, wn = _workspace(workspace, b, hq, hkv, d, bs, w, partition_size, q.device)
     st = lib.pa_store_decode(out.data_ptr(), qp, qs, kp, ks, vp, vs, slot_mapping.data_ptr(),
                              k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), w,
                              context_lens.data_ptr(), b, hq, hkv, d, bs, n, float(scale),
@@ -244,4 +263,116 @@ def pa_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seq
                                cu_seqlens_k.data_ptr(), int(max_seqlen_q), int(max_seqlen_k), bt_ptr, w,
                                bsq, hq, hkv, d, bs, n, float(scale), _dtype_code(q), _stream(q))
     _check("pa_prefill_varlen", st)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# E4M3 (fp8) caches: one-byte codes with a per-tensor scale for K and for V;
+# queries, new key/value rows and outputs are bf16.
+# ---------------------------------------------------------------------------
+
+def pa_store_kvcache_fp8(key, value, k_cache, v_cache, slot_mapping, k_scale, v_scale) -> None:
+    """Quantise bf16 key/value rows [T, H_kv, D] (x / scale, nearest E4M3
+    code) and scatter them into the fp8 caches at slot_mapping."""
+    import torch
+    lib = load()
+    n, bs, hkv, d = _fp8_cache_dims(k_cache, v_cache)
+    _int32(slot_mapping, "slot_mapping")
+    t = int(slot_mapping.shape[0])
+    kp, ks = _rows(key, "key")
+    vp, vs = _rows(value, "value")
+    _require(key.shape[0] == t and value.shape[0] == t, "key/value rows != len(slot_mapping)")
+    _require(tuple(key.shape[1:]) == (hkv, d) and tuple(value.shape[1:]) == (hkv, d), "key/value head shape")
+    _require(key.dtype == value.dtype == torch.bfloat16, "key/value must be bf16")
+    st = lib.pa_store_kvcache_fp8(kp, ks, vp, vs, k_cache.data_ptr(), v_cache.data_ptr(),
+                                  slot_mapping.data_ptr(), t, n, bs, hkv, d, float(k_scale),
+                                  float(v_scale), PA_BF16, _stream(k_cache))
+    _check("pa_store_kvcache_fp8", st)
+
+
+def pa_decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale, out=None,
+                  workspace=None, partition_size=0):
+    """Paged GQA decode over fp8 caches. q [B, H_q, D] bf16; returns bf16 out."""
+    import torch
+    lib = load()
+    n, bs, hkv, d = _fp8_cache_dims(k_cache, v_cache)
+    _int32(block_tables, "block_tables")
+    _int32(context_lens, "context_lens")
+    qp, qs = _rows(q, "q")
+    b, hq = int(q.shape[0]), int(q.shape[1])
+    _require(q.shape[2] == d and q.dtype == torch.bfloat16, "q shape/dtype")
+    _require(block_tables.dim() == 2 and block_tables.shape[0] == b, "block_tables must be [B, W]")
+    _require(context_lens.shape == (b,), "context_lens must be [B]")
+    w = int(block_tables.shape[1])
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=q.dtype, device=q.device)
+    _require(out.is_contiguous() and tuple(out.shape) == (b, hq, d) and out.dtype == q.dtype, "out")
+    wp, wn = _workspace(workspace, b, hq, hkv, d, bs, w, partition_size, q.device)
+    st = lib.pa_decode_fp8(out.data_ptr(), qp, qs, k_cache.data_ptr(), v_cache.data_ptr(),
+                           block_tables.data_ptr(), w, context_lens.data_ptr(), b, hq, hkv, d, bs, n,
+                           float(scale), float(k_scale), float(v_scale), int(partition_size), PA_BF16,
+                           wp, wn, _stream(q))
+    _check("pa_decode_fp8", st)
+    return out
+
+
+def pa_store_decode_fp8(q, key, value, slot_mapping, k_cache, v_cache, block_tables, context_lens,
+                        scale, k_scale, v_scale, out=None, workspace=None, partition_size=0):
+    """pa_store_kvcache_fp8 + pa_decode_fp8 in one launch (slot_mapping[b]
+    is -1 or the slot of position context_lens[b] - 1)."""
+    import torch
+    lib = load()
+    n, bs, hkv, d = _fp8_cache_dims(k_cache, v_cache)
+    _int32(block_tables, "block_tables")
+    _int32(context_lens, "context_lens")
+    _int32(slot_mapping, "slot_mapping")
+    qp, qs = _rows(q, "q")
+    kp, ks = _rows(key, "key")
+    vp, vs = _rows(value, "value")
+    b, hq = int(q.shape[0]), int(q.shape[1])
+    _require(q.shape[2] == d and q.dtype == torch.bfloat16, "q shape/dtype")
+    _require(tuple(key.shape) == (b, hkv, d) and tuple(value.shape) == (b, hkv, d), "key/value shape")
+    _require(key.dtype == value.dtype == torch.bfloat16, "key/value must be bf16")
+    _require(slot_mapping.shape == (b,), "slot_mapping must be [B]")
+    _require(block_tables.dim() == 2 and block_tables.shape[0] == b, "block_tables must be [B, W]")
+    _require(context_lens.shape == (b,), "context_lens must be [B]")
+    w = int(block_tables.shape[1])
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=q.dtype, device=q.device)
+    _require(out.is_contiguous() and tuple(out.shape) == (b, hq, d) and out.dtype == q.dtype, "out")
+    wp, wn = _workspace(workspace, b, hq, hkv, d, bs, w, partition_size, q.device)
+    st = lib.pa_store_decode_fp8(out.data_ptr(), qp, qs, kp, ks, vp, vs, slot_mapping.data_ptr(),
+                                 k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), w,
+                                 context_lens.data_ptr(), b, hq, hkv, d, bs, n, float(scale),
+                                 float(k_scale), float(v_scale), int(partition_size), PA_BF16, wp, wn,
+                                 _stream(q))
+    _check("pa_store_decode_fp8", st)
+    return out
+
+
+def pa_prefill_varlen_fp8(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                          block_tables, scale, k_scale, v_scale, out=None):
+    """Packed varlen causal prefill whose keys and values are read from fp8
+    paged caches through block_tables. q [Tq, H_q, D] bf16."""
+    import torch
+    lib = load()
+    _int32(cu_seqlens_q, "cu_seqlens_q")
+    _int32(cu_seqlens_k, "cu_seqlens_k")
+    _int32(block_tables, "block_tables")
+    qp, qs = _rows(q, "q")
+    tq, hq = int(q.shape[0]), int(q.shape[1])
+    bsq = int(cu_seqlens_q.shape[0]) - 1
+    _require(cu_seqlens_k.shape == cu_seqlens_q.shape, "cu_seqlens_k must match cu_seqlens_q")
+    n, bs, hkv, d = _fp8_cache_dims(k_cache, v_cache)
+    _require(block_tables.dim() == 2 and block_tables.shape[0] == bsq, "block_tables must be [B, W]")
+    _require(q.shape[2] == d and q.dtype == torch.bfloat16, "q shape/dtype")
+    if out is None:
+        out = torch.empty((tq, hq, d), dtype=q.dtype, device=q.device)
+    _require(out.is_contiguous() and tuple(out.shape) == (tq, hq, d) and out.dtype == q.dtype, "out")
+    st = lib.pa_prefill_varlen_fp8(out.data_ptr(), qp, qs, tq, k_cache.data_ptr(), v_cache.data_ptr(),
+                                   cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), int(max_seqlen_q),
+                                   int(max_seqlen_k), block_tables.data_ptr(), int(block_tables.shape[1]),
+                                   bsq, hq, hkv, d, bs, n, float(scale), float(k_scale), float(v_scale),
+                                   PA_BF16, _stream(q))
+    _check("pa_prefill_varlen_fp8", st)
     return out

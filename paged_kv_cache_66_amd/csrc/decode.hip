@@ -132,16 +132,53 @@ template <> struct QSlice<BF16Tag> {
   }
 };
 
+// fp8 cache: the query stays bf16 (pairs as for a bf16 cache); each pair of
+// E4M3 codes is widened to a bf16 pair (exact) and fed to v_dot2_f32_bf16.
+template <> struct QSlice<Fp8Tag> {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  uint32_t v[8];
+  __device__ __forceinline__ void load(const Vec16& x0, const Vec16& x1) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      v[w] = x0.w[w];
+      v[4 + w] = x1.w[w];
+    }
+  }
+  __device__ __forceinline__ static float dot2(uint32_t q, uint32_t k, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q), __builtin_bit_cast(bf16x2_t, k),
+                                           acc, false);
+  }
+  __device__ __forceinline__ float dot(const Vec8& k0, const Vec8& k1) const {
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      acc = dot2(v[2 * w], e4m3x2_to_bf16x2<false>(k0.w[w]), acc);
+      acc = dot2(v[2 * w + 1], e4m3x2_to_bf16x2<true>(k0.w[w]), acc);
+    }
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      acc = dot2(v[4 + 2 * w], e4m3x2_to_bf16x2<false>(k1.w[w]), acc);
+      acc = dot2(v[4 + 2 * w + 1], e4m3x2_to_bf16x2<true>(k1.w[w]), acc);
+    }
+    return acc;
+  }
+};
+
 // Dynamic LDS layout of the partition kernel (in 4-byte words):
 //   [0, G * max(partition, 4 * D))   scores, then reused for the wave reduction
 //   then G maxima, G sums, then the partition's block ids.
 //
+// T is the cache element type (fp32, bf16, or E4M3 codes with bf16 queries
+// and outputs). For an E4M3 cache the score scale already carries k_scale and
+// the output is multiplied by v_scale.
+//
 // With FUSED the step's new K/V rows are scattered by this kernel as well
 // (one launch instead of pa_store_kvcache + pa_decode): the workgroup whose
-// partition holds position context_len - 1 of a sequence reads that row from
-// the new key/value inputs instead of the cache and writes its kv head slice
-// to the cache at slot_mapping[b]. The caller guarantees that slot is the
-// slot of position context_len - 1 (or -1: no store, row read from the cache).
+// partition holds position context_len - 1 of a sequence writes that row's
+// kv head slice to the cache at slot_mapping[b] (E4M3 caches: quantised with
+// k_scale / v_scale first) and takes the row from the new key/value inputs
+// instead of the cache. The caller guarantees that slot is the slot of
+// position context_len - 1 (or -1: no store, row read from the cache).
 template <typename T, int D, int G, bool FUSED>
 __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
     void* __restrict__ out, const char* __restrict__ q, int64_t q_stride_bytes,
@@ -151,12 +188,18 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
     int32_t log2_bs, float scale_log2, int32_t partition, int32_t num_partitions,
     int32_t score_words, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
     const char* __restrict__ new_k, int64_t new_k_stride_bytes, const char* __restrict__ new_v,
-    int64_t new_v_stride_bytes, const int32_t* __restrict__ slot_mapping) {
+    int64_t new_v_stride_bytes, const int32_t* __restrict__ slot_mapping, float k_scale,
+    float v_scale) {
   using E = Elem<T>;
-  constexpr int EPV = E::kPerVec;    // elements per 16-byte vector
-  constexpr int EB = E::kBytes;      // bytes per element
+  using Vec = typename E::Vec;
+  constexpr bool kFp8 = E::kBytes == 1;
+  constexpr int EPV = E::kPerVec;    // cache elements per lane vector
+  constexpr int EB = E::kBytes;      // bytes per cache element
+  constexpr int QB = E::kQBytes;     // bytes per query / output element
+  constexpr int VB = EPV * EB;       // bytes per lane vector (16, or 8 for fp8)
+  constexpr int kUnroll = 128 / VB;  // loads in flight per lane and loop trip
   // score pass: a (token, kv head) row is spread over LPT1 lanes holding two
-  // 16-byte vectors each (fewer lanes per row -> fewer reduction steps)
+  // vectors each (fewer lanes per row -> fewer reduction steps)
   constexpr int LPT1 = D / (2 * EPV);
   constexpr int TPW1 = 64 / LPT1;
   constexpr int STEP1 = kWaves * TPW1;
@@ -194,7 +237,7 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
         const int h = g * G + i / D;
         const int d = i % D;
         const int64_t o = (static_cast<int64_t>(b) * num_q_heads + h) * D + d;
-        if constexpr (EB == 2) {
+        if constexpr (QB == 2) {
           reinterpret_cast<uint16_t*>(out)[o] = 0;
         } else {
           reinterpret_cast<float*>(out)[o] = 0.f;
@@ -217,17 +260,18 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   const int li1 = lane % LPT1;
   QSlice<T> qs[G];
   {
+    // the query elements that match the lane's two K vectors: 16 bytes each
     const char* qrow = q + static_cast<int64_t>(b) * q_stride_bytes;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const char* qh = qrow + static_cast<int64_t>(g * G + h) * D * EB;
-      qs[h].load(load16(qh + li1 * 16), load16(qh + (LPT1 + li1) * 16));
+      const char* qh = qrow + static_cast<int64_t>(g * G + h) * D * QB;
+      qs[h].load(load16(qh + li1 * EPV * QB), load16(qh + (LPT1 + li1) * EPV * QB));
     }
   }
   __syncthreads();
 
   const uint64_t row_bytes = static_cast<uint64_t>(num_kv_heads) * D * EB;
-  const int64_t lane_off = static_cast<int64_t>(g) * D * EB + li * 16;
+  const int64_t lane_off = static_cast<int64_t>(g) * D * EB + li * VB;
   const char* vbase = v_cache + lane_off;
   const int my_row = wave * TPW + grp;  // row of this lane within a load step
 
@@ -239,42 +283,61 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   };
 
   // The step's new row (fused scatter): local index in this partition, or -1
-  // when it is not here or not stored. Its head slice is copied to the cache
-  // slot once, here; the loops below read it from the inputs (so nothing in
-  // this launch reads the row it writes), selecting the address per row.
+  // when it is not here or not stored. Its head slice is written to the cache
+  // slot once, here, and nothing in this launch reads it back from there:
+  // 16-bit and fp32 caches take the row from the inputs by selecting the
+  // address per row; an E4M3 cache needs the quantised codes, so every lane
+  // quantises its own slices of the new row into registers and selects the
+  // data instead.
   int new_tl = -1;
   const char* nk_row = nullptr;
   const char* nv_row = nullptr;
+  Vec nk0{}, nk1{}, nv{};
   if constexpr (FUSED) {
     const int slot = slot_mapping[b];
     if (slot >= 0 && n - 1 >= t0 && n - 1 < t1) {
       new_tl = n - 1 - t0;
-      nk_row = new_k + static_cast<int64_t>(b) * new_k_stride_bytes + static_cast<int64_t>(g) * D * EB;
-      nv_row = new_v + static_cast<int64_t>(b) * new_v_stride_bytes + static_cast<int64_t>(g) * D * EB;
+      nk_row = new_k + static_cast<int64_t>(b) * new_k_stride_bytes + static_cast<int64_t>(g) * D * QB;
+      nv_row = new_v + static_cast<int64_t>(b) * new_v_stride_bytes + static_cast<int64_t>(g) * D * QB;
       const int64_t dst = static_cast<int64_t>(slot) * static_cast<int64_t>(row_bytes) +
                           static_cast<int64_t>(g) * D * EB;
-      constexpr int kVecs = D * EB / 16;  // 16-byte vectors per head slice
-      if (tid < kVecs) store16(k_cache + dst + tid * 16, load16(nk_row + tid * 16));
-      else if (tid < 2 * kVecs) store16(v_cache + dst + (tid - kVecs) * 16, load16(nv_row + (tid - kVecs) * 16));
+      constexpr int kVecs = D * QB / 16;  // 16-byte input vectors per head slice
+      if constexpr (kFp8) {
+        if (tid < kVecs) store8(k_cache + dst + tid * 8, quantize8(load16(nk_row + tid * 16), k_scale));
+        else if (tid < 2 * kVecs)
+          store8(v_cache + dst + (tid - kVecs) * 8, quantize8(load16(nv_row + (tid - kVecs) * 16), v_scale));
+        nk0 = quantize8(load16(nk_row + li1 * 16), k_scale);
+        nk1 = quantize8(load16(nk_row + (LPT1 + li1) * 16), k_scale);
+        nv = quantize8(load16(nv_row + li * 16), v_scale);
+      } else {
+        if (tid < kVecs) store16(k_cache + dst + tid * 16, load16(nk_row + tid * 16));
+        else if (tid < 2 * kVecs) store16(v_cache + dst + (tid - kVecs) * 16, load16(nv_row + (tid - kVecs) * 16));
+      }
     }
   }
 
   // phase 1: raw scores q . k (the scale is applied once per score in phase 2)
-  const char* kbase1 = k_cache + static_cast<int64_t>(g) * D * EB + li1 * 16;
+  const char* kbase1 = k_cache + static_cast<int64_t>(g) * D * EB + li1 * VB;
   const int my_row1 = wave * TPW1 + grp1;
   for (int base = 0; base < ntok; base += STEP1 * kUnroll) {
-    Vec16 k0[kUnroll], k1[kUnroll];
+    Vec k0[kUnroll], k1[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int tl = base + u * STEP1 + my_row1;
       if (tl < ntok) {
         const char* r = kbase1 + row_off(tl);
-        if constexpr (FUSED) r = tl == new_tl ? nk_row + li1 * 16 : r;
-        k0[u] = load16_nt(r);
-        k1[u] = load16_nt(r + LPT1 * 16);
+        if constexpr (FUSED && !kFp8) r = tl == new_tl ? nk_row + li1 * 16 : r;
+        k0[u] = E::load_nt(r);
+        k1[u] = E::load_nt(r + LPT1 * VB);
+        if constexpr (FUSED && kFp8) {
+          if (tl == new_tl) {
+            k0[u] = nk0;
+            k1[u] = nk1;
+          }
+        }
       } else {
-        k0[u] = Vec16{{0u, 0u, 0u, 0u}};
-        k1[u] = k0[u];
+        k0[u] = Vec{};
+        k1[u] = Vec{};
       }
     }
 #pragma unroll
@@ -320,16 +383,19 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
     for (int e = 0; e < EPV; ++e) acc[h][e] = 0.f;
 
   for (int base = 0; base < ntok; base += STEP * kUnroll) {
-    Vec16 vv[kUnroll];
+    Vec vv[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int tl = base + u * STEP + my_row;
       if (tl < ntok) {
         const char* r = vbase + row_off(tl);
-        if constexpr (FUSED) r = tl == new_tl ? nv_row + li * 16 : r;
-        vv[u] = load16_nt(r);
+        if constexpr (FUSED && !kFp8) r = tl == new_tl ? nv_row + li * 16 : r;
+        vv[u] = E::load_nt(r);
+        if constexpr (FUSED && kFp8) {
+          if (tl == new_tl) vv[u] = nv;
+        }
       } else {
-        vv[u] = Vec16{{0u, 0u, 0u, 0u}};
+        vv[u] = Vec{};
       }
     }
 #pragma unroll
@@ -374,11 +440,12 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
     float v = s_red[(0 * G + h) * D + d];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) v += s_red[(w * G + h) * D + d];
+    if constexpr (kFp8) v *= v_scale;
     const int qh = g * G + h;
     if (single) {
       const float o = v / s_sum[h];
       const int64_t oi = (static_cast<int64_t>(b) * num_q_heads + qh) * D + d;
-      if constexpr (EB == 2) {
+      if constexpr (QB == 2) {
         reinterpret_cast<uint16_t*>(out)[oi] = static_cast<uint16_t>(f32_to_bf16_bits(o));
       } else {
         reinterpret_cast<float*>(out)[oi] = o;
@@ -447,7 +514,7 @@ __global__ void __launch_bounds__(64) decode_reduce_kernel(
   const int64_t ob = (static_cast<int64_t>(b) * num_q_heads + h) * D;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    if constexpr (Elem<T>::kBytes == 2) {
+    if constexpr (Elem<T>::kQBytes == 2) {
       reinterpret_cast<uint16_t*>(out)[ob + k * 64 + lane] = static_cast<uint16_t>(f32_to_bf16_bits(o[k]));
     } else {
       reinterpret_cast<float*>(out)[ob + k * 64 + lane] = o[k];
@@ -457,22 +524,24 @@ __global__ void __launch_bounds__(64) decode_reduce_kernel(
 
 template <typename T, int D, int G, bool FUSED>
 hipError_t launch_decode_typed(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int EB = Elem<T>::kBytes;
+  constexpr int QB = Elem<T>::kQBytes;
   int log2_bs = 0;
   while ((1 << log2_bs) < a.block_size) ++log2_bs;
   const int score_words = G * (a.partition > 4 * D ? a.partition : 4 * D);
   const int max_ids = a.partition / (a.block_size < a.partition ? a.block_size : a.partition) + 2;
   const size_t lds = static_cast<size_t>(score_words + 2 * G + max_ids) * 4;
-  const float scale_log2 = a.scale * kLog2e;
+  // an E4M3 cache holds K / k_scale: the score scale absorbs k_scale
+  const float scale_log2 = a.scale * (Elem<T>::kBytes == 1 ? a.k_scale : 1.f) * kLog2e;
   dim3 grid(a.num_partitions * a.num_kv_heads * a.num_seqs);
   hipLaunchKernelGGL((decode_partition_kernel<T, D, G, FUSED>), grid, dim3(kThreads), lds, stream,
-                     a.out, static_cast<const char*>(a.q), a.q_stride * EB,
+                     a.out, static_cast<const char*>(a.q), a.q_stride * QB,
                      static_cast<char*>(const_cast<void*>(a.k_cache)),
                      static_cast<char*>(const_cast<void*>(a.v_cache)), a.block_tables, a.max_blocks,
                      a.context_lens, a.num_q_heads, a.num_kv_heads, log2_bs, scale_log2, a.partition,
                      a.num_partitions, score_words, a.ws_acc, a.ws_ml,
-                     static_cast<const char*>(a.new_k), a.new_k_stride * EB,
-                     static_cast<const char*>(a.new_v), a.new_v_stride * EB, a.slot_mapping);
+                     static_cast<const char*>(a.new_k), a.new_k_stride * QB,
+                     static_cast<const char*>(a.new_v), a.new_v_stride * QB, a.slot_mapping,
+                     a.k_scale, a.v_scale);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.num_partitions == 1) return err;
   hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3(a.num_q_heads, a.num_seqs), dim3(64), 0,
@@ -523,12 +592,18 @@ int32_t decode_partition_tokens(int32_t requested, int32_t num_seqs, int32_t num
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  if (a.bf16) {
-    return a.head_dim == 64 ? dispatch_fused<BF16Tag, 64>(a, stream)
-                            : dispatch_fused<BF16Tag, 128>(a, stream);
+  switch (a.kv) {
+    case KvFormat::kBf16:
+      return a.head_dim == 64 ? dispatch_fused<BF16Tag, 64>(a, stream)
+                              : dispatch_fused<BF16Tag, 128>(a, stream);
+    case KvFormat::kFp8E4m3:
+      return a.head_dim == 64 ? dispatch_fused<Fp8Tag, 64>(a, stream)
+                              : dispatch_fused<Fp8Tag, 128>(a, stream);
+    case KvFormat::kF32:
+      return a.head_dim == 64 ? dispatch_fused<float, 64>(a, stream)
+                              : dispatch_fused<float, 128>(a, stream);
   }
-  return a.head_dim == 64 ? dispatch_fused<float, 64>(a, stream)
-                          : dispatch_fused<float, 128>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa

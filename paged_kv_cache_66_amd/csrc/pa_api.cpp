@@ -22,6 +22,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int elem_bytes(pa_dtype d) { return d == PA_BF16 ? 2 : 4; }
 bool dtype_ok(int d) { return d == PA_F32 || d == PA_BF16; }
 bool group_ok(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 
 pa_status check_head_layout(int32_t head_dim, int32_t block_size, int32_t num_blocks) {
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
@@ -54,31 +55,14 @@ int64_t num_partitions(int32_t partition, int32_t block_size, int32_t max_blocks
   return ceil_div(static_cast<int64_t>(max_blocks) * block_size, partition);
 }
 
-}  // namespace
 
-extern "C" {
 
-const char* pa_status_string(int status) {
-  switch (status) {
-    case PA_OK: return "ok";
-    case PA_ERR_NULL: return "null pointer argument";
-    case PA_ERR_SHAPE: return "invalid or inconsistent size";
-    case PA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, group size, dtype or mode";
-    case PA_ERR_ALIGN: return "pointer or row stride not 16-byte aligned";
-    case PA_ERR_WORKSPACE: return "workspace missing or too small";
-    case PA_ERR_HIP: return "HIP runtime error";
-    default: return "unknown status";
-  }
-}
-
-const char* pa_version(void) { return "paged_kv_cache_66_amd 0.1.0 (gfx950)"; }
-
-pa_status pa_store_kvcache(const void* key, int64_t key_row_stride, const void* value,
-                           int64_t value_row_stride, void* k_cache, void* v_cache,
-                           const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
-                           int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
-                           pa_dtype dtype, void* stream) {
-  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+// Shared by pa_store_kvcache and pa_store_kvcache_fp8 (dtype already checked).
+pa_status store_common(const void* key, int64_t key_row_stride, const void* value,
+                       int64_t value_row_stride, void* k_cache, void* v_cache,
+                       const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                       int32_t block_size, int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                       bool fp8, float k_scale, float v_scale, void* stream) {
   if (num_tokens < 0 || num_kv_heads <= 0) return PA_ERR_SHAPE;
   pa_status st = check_head_layout(head_dim, block_size, num_blocks);
   if (st != PA_OK) return st;
@@ -92,26 +76,9 @@ pa_status pa_store_kvcache(const void* key, int64_t key_row_stride, const void* 
   if ((st = check_rows(value, value_row_stride, row, eb)) != PA_OK) return st;
   if (row * eb > INT32_MAX) return PA_ERR_SHAPE;
   pa::StoreArgs a{key, key_row_stride * eb, value, value_row_stride * eb, k_cache, v_cache,
-                  slot_mapping, num_tokens, static_cast<int32_t>(row * eb)};
+                  slot_mapping, num_tokens, static_cast<int32_t>(row * eb), fp8, k_scale, v_scale};
   return pa::launch_store(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
-
-size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
-                                int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
-      head_dim <= 0 || !is_pow2(block_size) || max_blocks_per_seq <= 0)
-    return 0;
-  const int32_t part = resolve_partition(partition_size, num_seqs, num_kv_heads,
-                                         num_q_heads / num_kv_heads, block_size, max_blocks_per_seq);
-  if (part <= 0) return 0;
-  const int64_t P = num_partitions(part, block_size, max_blocks_per_seq);
-  if (P <= 1) return 0;
-  const int64_t slots = static_cast<int64_t>(num_seqs) * num_q_heads * P;
-  return static_cast<size_t>(slots * head_dim * 4 + slots * 2 * 4);
-}
-
-namespace {
 
 // Validation and argument packing shared by pa_decode and pa_store_decode.
 pa_status prepare_decode(void* out, const void* q, int64_t q_row_stride, const void* k_cache,
@@ -119,9 +86,12 @@ pa_status prepare_decode(void* out, const void* q, int64_t q_row_stride, const v
                          int32_t max_blocks_per_seq, const int32_t* context_lens,
                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                          int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
-                         int32_t partition_size, pa_dtype dtype, void* workspace,
-                         size_t workspace_bytes, pa::DecodeArgs* a) {
+                         int32_t partition_size, pa_dtype dtype, pa::KvFormat kv, float k_scale,
+                         float v_scale, void* workspace, size_t workspace_bytes,
+                         pa::DecodeArgs* a) {
   if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  if (kv == pa::KvFormat::kFp8E4m3 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (!scale_ok(k_scale) || !scale_ok(v_scale)) return PA_ERR_SHAPE;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0)
     return PA_ERR_SHAPE;
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
@@ -130,7 +100,7 @@ pa_status prepare_decode(void* out, const void* q, int64_t q_row_stride, const v
   if (num_seqs > kMaxGridYZ || num_kv_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
   pa_status st = check_head_layout(head_dim, block_size, num_blocks);
   if (st != PA_OK) return st;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return PA_ERR_SHAPE;
+  if (!scale_ok(scale)) return PA_ERR_SHAPE;
   const int32_t part = resolve_partition(partition_size, num_seqs, num_kv_heads, G, block_size,
                                          max_blocks_per_seq);
   if (part <= 0) return PA_ERR_UNSUPPORTED;
@@ -175,65 +145,57 @@ pa_status prepare_decode(void* out, const void* q, int64_t q_row_stride, const v
   a->num_partitions = static_cast<int32_t>(P);
   a->ws_acc = ws_acc;
   a->ws_ml = ws_ml;
-  a->bf16 = dtype == PA_BF16;
+  a->kv = kv;
+  a->k_scale = k_scale;
+  a->v_scale = v_scale;
   return PA_OK;
 }
 
-}  // namespace
-
-pa_status pa_decode(void* out, const void* q, int64_t q_row_stride, const void* k_cache,
-                    const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                    float scale, int32_t partition_size, pa_dtype dtype, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+pa_status decode_common(void* out, const void* q, int64_t q_row_stride, const void* key,
+                        int64_t key_row_stride, const void* value, int64_t value_row_stride,
+                        const int32_t* slot_mapping, bool fused, const void* k_cache,
+                        const void* v_cache, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                        int32_t partition_size, pa_dtype dtype, pa::KvFormat kv, float k_scale,
+                        float v_scale, void* workspace, size_t workspace_bytes, void* stream) {
   pa::DecodeArgs a;
   pa_status st = prepare_decode(out, q, q_row_stride, k_cache, v_cache, block_tables,
                                 max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
                                 num_kv_heads, head_dim, block_size, num_blocks, scale,
-                                partition_size, dtype, workspace, workspace_bytes, &a);
+                                partition_size, dtype, kv, k_scale, v_scale, workspace,
+                                workspace_bytes, &a);
   if (st != PA_OK || num_seqs == 0) return st;
+  if (fused) {
+    if (key == nullptr || value == nullptr || slot_mapping == nullptr) return PA_ERR_NULL;
+    const int eb = elem_bytes(dtype);
+    const int64_t row = static_cast<int64_t>(num_kv_heads) * head_dim;
+    if ((st = check_rows(key, key_row_stride, row, eb)) != PA_OK) return st;
+    if ((st = check_rows(value, value_row_stride, row, eb)) != PA_OK) return st;
+    a.new_k = key;
+    a.new_k_stride = key_row_stride;
+    a.new_v = value;
+    a.new_v_stride = value_row_stride;
+    a.slot_mapping = slot_mapping;
+  }
   return pa::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-pa_status pa_store_decode(void* out, const void* q, int64_t q_row_stride, const void* key,
-                          int64_t key_row_stride, const void* value, int64_t value_row_stride,
-                          const int32_t* slot_mapping, void* k_cache, void* v_cache,
-                          const int32_t* block_tables, int32_t max_blocks_per_seq,
-                          const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                          int32_t num_blocks, float scale, int32_t partition_size,
-                          pa_dtype dtype, void* workspace, size_t workspace_bytes,
-                          void* stream) {
-  pa::DecodeArgs a;
-  pa_status st = prepare_decode(out, q, q_row_stride, k_cache, v_cache, block_tables,
-                                max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
-                                num_kv_heads, head_dim, block_size, num_blocks, scale,
-                                partition_size, dtype, workspace, workspace_bytes, &a);
-  if (st != PA_OK || num_seqs == 0) return st;
-  if (key == nullptr || value == nullptr || slot_mapping == nullptr) return PA_ERR_NULL;
-  const int eb = elem_bytes(dtype);
-  const int64_t row = static_cast<int64_t>(num_kv_heads) * head_dim;
-  if ((st = check_rows(key, key_row_stride, row, eb)) != PA_OK) return st;
-  if ((st = check_rows(value, value_row_stride, row, eb)) != PA_OK) return st;
-  a.new_k = key;
-  a.new_k_stride = key_row_stride;
-  a.new_v = value;
-  a.new_v_stride = value_row_stride;
-  a.slot_mapping = slot_mapping;
-  return pa::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
+pa::KvFormat kv_of(pa_dtype dtype) {
+  return dtype == PA_BF16 ? pa::KvFormat::kBf16 : pa::KvFormat::kF32;
 }
 
-pa_status pa_prefill_varlen(void* out, const void* q, int64_t q_row_stride, int32_t total_q,
-                            const void* k, int64_t k_row_stride, const void* v,
-                            int64_t v_row_stride, const int32_t* cu_seqlens_q,
-                            const int32_t* cu_seqlens_k, int32_t max_seqlen_q,
-                            int32_t max_seqlen_k, const int32_t* block_tables,
-                            int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
-                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                            int32_t num_blocks, float scale, pa_dtype dtype, void* stream) {
-  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+pa_status prefill_common(void* out, const void* q, int64_t q_row_stride, int32_t total_q,
+                         const void* k, int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                         int32_t max_seqlen_q, int32_t max_seqlen_k, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t num_blocks, float scale, pa_dtype dtype, bool fp8, float k_scale,
+                         float v_scale, void* stream) {
   if (dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (!scale_ok(k_scale) || !scale_ok(v_scale)) return PA_ERR_SHAPE;
   if (total_q < 0 || num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_q_heads <= 0 ||
       num_kv_heads <= 0)
     return PA_ERR_SHAPE;
@@ -242,7 +204,7 @@ pa_status pa_prefill_varlen(void* out, const void* q, int64_t q_row_stride, int3
   if (!group_ok(G)) return PA_ERR_UNSUPPORTED;
   if (num_seqs > kMaxGridYZ || num_kv_heads > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return PA_ERR_SHAPE;
+  if (!scale_ok(scale)) return PA_ERR_SHAPE;
   const int64_t row = static_cast<int64_t>(num_kv_heads) * head_dim;
   const bool paged = block_tables != nullptr;
   pa_status st;
@@ -288,7 +250,158 @@ pa_status pa_prefill_varlen(void* out, const void* q, int64_t q_row_stride, int3
   a.head_dim = head_dim;
   a.block_size = paged ? block_size : 1;
   a.scale = scale;
+  a.fp8 = fp8;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   return pa::launch_prefill(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "null pointer argument";
+    case PA_ERR_SHAPE: return "invalid or inconsistent size";
+    case PA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, group size, dtype or mode";
+    case PA_ERR_ALIGN: return "pointer or row stride not 16-byte aligned";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* pa_version(void) { return "paged_kv_cache_66_amd 0.1.0 (gfx950)"; }
+
+pa_status pa_store_kvcache(const void* key, int64_t key_row_stride, const void* value,
+                           int64_t value_row_stride, void* k_cache, void* v_cache,
+                           const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                           int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                           pa_dtype dtype, void* stream) {
+  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  return store_common(key, key_row_stride, value, value_row_stride, k_cache, v_cache, slot_mapping,
+                      num_tokens, num_blocks, block_size, num_kv_heads, head_dim, dtype, false, 1.f,
+                      1.f, stream);
+}
+
+pa_status pa_store_kvcache_fp8(const void* key, int64_t key_row_stride, const void* value,
+                               int64_t value_row_stride, void* k_cache, void* v_cache,
+                               const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                               int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                               float k_scale, float v_scale, pa_dtype dtype, void* stream) {
+  if (dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (!scale_ok(k_scale) || !scale_ok(v_scale)) return PA_ERR_SHAPE;
+  return store_common(key, key_row_stride, value, value_row_stride, k_cache, v_cache, slot_mapping,
+                      num_tokens, num_blocks, block_size, num_kv_heads, head_dim, dtype, true,
+                      k_scale, v_scale, stream);
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+      head_dim <= 0 || !is_pow2(block_size) || max_blocks_per_seq <= 0)
+    return 0;
+  const int32_t part = resolve_partition(partition_size, num_seqs, num_kv_heads,
+                                         num_q_heads / num_kv_heads, block_size, max_blocks_per_seq);
+  if (part <= 0) return 0;
+  const int64_t P = num_partitions(part, block_size, max_blocks_per_seq);
+  if (P <= 1) return 0;
+  const int64_t slots = static_cast<int64_t>(num_seqs) * num_q_heads * P;
+  return static_cast<size_t>(slots * head_dim * 4 + slots * 2 * 4);
+}
+
+pa_status pa_decode(void* out, const void* q, int64_t q_row_stride, const void* k_cache,
+                    const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                    float scale, int32_t partition_size, pa_dtype dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return decode_common(out, q, q_row_stride, nullptr, 0, nullptr, 0, nullptr, false, k_cache,
+                       v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                       partition_size, dtype, kv_of(dtype), 1.f, 1.f, workspace, workspace_bytes,
+                       stream);
+}
+
+pa_status pa_store_decode(void* out, const void* q, int64_t q_row_stride, const void* key,
+                          int64_t key_row_stride, const void* value, int64_t value_row_stride,
+                          const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          int32_t num_blocks, float scale, int32_t partition_size,
+                          pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return decode_common(out, q, q_row_stride, key, key_row_stride, value, value_row_stride,
+                       slot_mapping, true, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, scale, partition_size, dtype, kv_of(dtype), 1.f, 1.f,
+                       workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_fp8(void* out, const void* q, int64_t q_row_stride, const void* k_cache,
+                        const void* v_cache, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                        float k_scale, float v_scale, int32_t partition_size, pa_dtype dtype,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(out, q, q_row_stride, nullptr, 0, nullptr, 0, nullptr, false, k_cache,
+                       v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                       partition_size, dtype, pa::KvFormat::kFp8E4m3, k_scale, v_scale,
+                       workspace, workspace_bytes, stream);
+}
+
+pa_status pa_store_decode_fp8(void* out, const void* q, int64_t q_row_stride, const void* key,
+                              int64_t key_row_stride, const void* value,
+                              int64_t value_row_stride, const int32_t* slot_mapping,
+                              void* k_cache, void* v_cache, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              float scale, float k_scale, float v_scale, int32_t partition_size,
+                              pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return decode_common(out, q, q_row_stride, key, key_row_stride, value, value_row_stride,
+                       slot_mapping, true, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, scale, partition_size, dtype, pa::KvFormat::kFp8E4m3, k_scale,
+                       v_scale, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_prefill_varlen(void* out, const void* q, int64_t q_row_stride, int32_t total_q,
+                            const void* k, int64_t k_row_stride, const void* v,
+                            int64_t v_row_stride, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, float scale, pa_dtype dtype, void* stream) {
+  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  return prefill_common(out, q, q_row_stride, total_q, k, k_row_stride, v, v_row_stride,
+                        cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, block_tables,
+                        max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                        block_size, num_blocks, scale, dtype, false, 1.f, 1.f, stream);
+}
+
+pa_status pa_prefill_varlen_fp8(void* out, const void* q, int64_t q_row_stride, int32_t total_q,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                float scale, float k_scale, float v_scale, pa_dtype dtype,
+                                void* stream) {
+  if (block_tables == nullptr) return PA_ERR_NULL;  // E4M3 data lives only in the paged caches
+  return prefill_common(out, q, q_row_stride, total_q, k_cache, 0, v_cache, 0, cu_seqlens_q,
+                        cu_seqlens_k, max_seqlen_q, max_seqlen_k, block_tables,
+                        max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                        block_size, num_blocks, scale, dtype, true, k_scale, v_scale, stream);
 }
 
 }  // extern "C"

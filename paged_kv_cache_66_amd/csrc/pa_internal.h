@@ -8,6 +8,11 @@
 
 namespace pa {
 
+// Storage format of the K/V caches. fp32 and bf16 caches share the element
+// type of the queries and outputs; an E4M3 cache holds one-byte codes with a
+// per-tensor scale each for K and V, next to bf16 queries and outputs.
+enum class KvFormat { kF32, kBf16, kFp8E4m3 };
+
 struct StoreArgs {
   const void* key;
   int64_t key_stride_bytes;
@@ -17,7 +22,10 @@ struct StoreArgs {
   void* v_cache;
   const int32_t* slot_mapping;
   int32_t num_tokens;
-  int32_t row_bytes;  // num_kv_heads * head_dim * element bytes
+  int32_t row_bytes;  // bytes of one input row: num_kv_heads * head_dim * input element bytes
+  bool fp8;           // quantise bf16 input rows to E4M3 cache rows (row_bytes / 2 each)
+  float k_scale;
+  float v_scale;
 };
 
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
@@ -41,7 +49,9 @@ struct DecodeArgs {
   int32_t num_partitions;  // max partitions per sequence (grid x)
   float* ws_acc;         // [B, H_q, P, D] when num_partitions > 1
   float* ws_ml;          // [B, H_q, P, 2]
-  bool bf16;
+  KvFormat kv;
+  float k_scale;         // E4M3 caches: stored code = K / k_scale (1 otherwise)
+  float v_scale;
   // fused scatter of the step's new rows (slot_mapping == nullptr: plain decode)
   const void* new_k;
   int64_t new_k_stride;  // elements
@@ -73,6 +83,9 @@ struct PrefillArgs {
   int32_t head_dim;
   int32_t block_size;
   float scale;
+  bool fp8;       // paged E4M3 caches (bf16 queries and outputs)
+  float k_scale;
+  float v_scale;
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

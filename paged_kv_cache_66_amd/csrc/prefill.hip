@@ -28,6 +28,9 @@
 // * K/V tiles are double-buffered in LDS: the next tile's rows travel from
 //   HBM into registers while the current tile is multiplied, and one barrier
 //   per tile separates the buffer writes from the reads.
+// * E4M3 caches (FP8): tiles travel as one-byte codes and are widened to bf16
+//   (exactly) on their way into LDS; k_scale joins the softmax scale and
+//   v_scale the final normalisation.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -74,13 +77,34 @@ __device__ __forceinline__ uint32_t half16(const Vec16& v, int j) {
   return (j & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-template <int D, int G>
+// Eight key / value elements as the tile loads carry them (bf16, or E4M3
+// codes) and their bf16 form for LDS.
+template <bool FP8> struct TileVec;
+template <> struct TileVec<false> {
+  using Vec = Vec16;
+  __device__ __forceinline__ static Vec load(const char* p) { return load16(p); }
+  __device__ __forceinline__ static Vec16 to_bf16(const Vec& v) { return v; }
+};
+template <> struct TileVec<true> {
+  using Vec = Vec8;
+  __device__ __forceinline__ static Vec load(const char* p) { return load8(p); }
+  __device__ __forceinline__ static Vec16 to_bf16(const Vec& v) {
+    return Vec16{{e4m3x2_to_bf16x2<false>(v.w[0]), e4m3x2_to_bf16x2<true>(v.w[0]),
+                  e4m3x2_to_bf16x2<false>(v.w[1]), e4m3x2_to_bf16x2<true>(v.w[1])}};
+  }
+};
+
+template <int D, int G, bool FP8>
 __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
     uint16_t* __restrict__ out, const char* __restrict__ q, int64_t q_stride_bytes,
     const char* __restrict__ k_cache, const char* __restrict__ v_cache, int64_t k_stride_bytes,
     int64_t v_stride_bytes, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
     const int32_t* __restrict__ block_tables, int32_t max_blocks, int32_t num_q_heads,
-    int32_t num_kv_heads, int32_t log2_bs, float scale_log2, int32_t max_qt) {
+    int32_t num_kv_heads, int32_t log2_bs, float scale_log2, int32_t max_qt, float v_scale) {
+  using TV = TileVec<FP8>;
+  using KVec = typename TV::Vec;
+  constexpr int KB = FP8 ? 1 : 2;  // bytes per cache element
+  constexpr int CB = 8 * KB;       // bytes per 8-element chunk
   constexpr int QT = kRows / G;    // queries per workgroup
   constexpr int KS = D / 32;       // MFMA k-steps over head_dim
   constexpr int DT = D / 16;       // 16-wide head_dim tiles of the output
@@ -165,7 +189,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   // the block table, or, without a table, from packed k / v tensors where key
   // t of sequence i is row cu_k[i] + t (row strides given by the caller).
   const bool paged = block_tables != nullptr;
-  const int64_t head_off = static_cast<int64_t>(g) * D * 2;
+  const int64_t head_off = static_cast<int64_t>(g) * D * KB;
   const int32_t* table = paged ? block_tables + static_cast<int64_t>(i) * max_blocks : nullptr;
   const int bs_mask = (1 << log2_bs) - 1;
   const int64_t k0_row = paged ? 0 : cu_k[i];
@@ -181,8 +205,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   };
 
   // ---- tile fetch into registers ----
-  Vec16 kreg[KLOADS];
-  Vec16 vreg[VK];
+  KVec kreg[KLOADS];
+  KVec vreg[VK];
   const int vkg = tid % VGROUPS;  // group of VK consecutive V rows of the item
   const int vdc = tid / VGROUPS;  // 16-byte chunk of the V item
   // Byte offsets of this thread's K and V vectors inside a contiguous tile
@@ -193,11 +217,11 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
 #pragma unroll
   for (int u = 0; u < KLOADS; ++u) {
     const int item = tid + u * kThreads;
-    koff[u] = static_cast<uint32_t>((item / KCH) * k_stride_bytes + (item % KCH) * 16);
+    koff[u] = static_cast<uint32_t>((item / KCH) * k_stride_bytes + (item % KCH) * CB);
   }
 #pragma unroll
   for (int e = 0; e < VK; ++e)
-    voff[e] = static_cast<uint32_t>((vkg * VK + e) * v_stride_bytes + vdc * 16);
+    voff[e] = static_cast<uint32_t>((vkg * VK + e) * v_stride_bytes + vdc * CB);
 
   auto fetch = [&](int kt0) {
     if (tile_contiguous) {
@@ -207,12 +231,12 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
 #pragma unroll
       for (int u = 0; u < KLOADS; ++u) {
         const int key = kt0 + (tid + u * kThreads) / KCH;
-        kreg[u] = key < Lk ? load16(kb + koff[u]) : Vec16{{0u, 0u, 0u, 0u}};
+        kreg[u] = key < Lk ? TV::load(kb + koff[u]) : KVec{};
       }
 #pragma unroll
       for (int e = 0; e < VK; ++e) {
         const int key = kt0 + vkg * VK + e;
-        vreg[e] = key < Lk ? load16(vb + voff[e]) : Vec16{{0u, 0u, 0u, 0u}};
+        vreg[e] = key < Lk ? TV::load(vb + voff[e]) : KVec{};
       }
       return;
     }
@@ -220,12 +244,12 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
     for (int u = 0; u < KLOADS; ++u) {
       const int item = tid + u * kThreads;
       const int key = kt0 + item / KCH;
-      kreg[u] = key < Lk ? load16(k_cache + row_addr(key) + (item % KCH) * 16) : Vec16{{0u, 0u, 0u, 0u}};
+      kreg[u] = key < Lk ? TV::load(k_cache + row_addr(key) + (item % KCH) * CB) : KVec{};
     }
 #pragma unroll
     for (int e = 0; e < VK; ++e) {
       const int key = kt0 + vkg * VK + e;
-      vreg[e] = key < Lk ? load16(v_cache + row_addr(key) + vdc * 16) : Vec16{{0u, 0u, 0u, 0u}};
+      vreg[e] = key < Lk ? TV::load(v_cache + row_addr(key) + vdc * CB) : KVec{};
     }
   };
   auto commit = [&](int buf) {
@@ -234,8 +258,11 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
       const int item = tid + u * kThreads;
       const int r = item / KCH;
       const int c = item % KCH;
-      *reinterpret_cast<Vec16*>(&sK[buf][r * KPITCH + c * 8]) = kreg[u];
+      *reinterpret_cast<Vec16*>(&sK[buf][r * KPITCH + c * 8]) = TV::to_bf16(kreg[u]);
     }
+    Vec16 vb16[VK];
+#pragma unroll
+    for (int e = 0; e < VK; ++e) vb16[e] = TV::to_bf16(vreg[e]);
     // V goes to LDS transposed: element j of the chunk is row vdc * 8 + j of
     // sV, and the VK keys of this item sit side by side in that row
 #pragma unroll
@@ -243,13 +270,13 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
       uint16_t* dst = &sV[buf][(vdc * 8 + j) * VPITCH + vkg * VK];
       if constexpr (VK == 4) {
         uint2 pk;
-        pk.x = half16(vreg[0], j) | (half16(vreg[1], j) << 16);
-        pk.y = half16(vreg[2], j) | (half16(vreg[3], j) << 16);
+        pk.x = half16(vb16[0], j) | (half16(vb16[1], j) << 16);
+        pk.y = half16(vb16[2], j) | (half16(vb16[3], j) << 16);
         *reinterpret_cast<uint2*>(dst) = pk;
       } else if constexpr (VK == 2) {
-        *reinterpret_cast<uint32_t*>(dst) = half16(vreg[0], j) | (half16(vreg[1], j) << 16);
+        *reinterpret_cast<uint32_t*>(dst) = half16(vb16[0], j) | (half16(vb16[1], j) << 16);
       } else {
-        *dst = static_cast<uint16_t>(half16(vreg[0], j));
+        *dst = static_cast<uint16_t>(half16(vb16[0], j));
       }
     }
   };
@@ -370,7 +397,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
     if (orow[t] < 0) continue;
-    const float inv = 1.f / lt;
+    const float inv = (FP8 ? v_scale : 1.f) / lt;
     uint16_t* orow_ptr = out + (static_cast<int64_t>(orow[t]) * num_q_heads + ohead[t]) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -382,8 +409,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   }
 }
 
-template <int D, int G>
+template <int D, int G, bool FP8>
 hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
+  constexpr int KB = FP8 ? 1 : 2;
   constexpr int QT = kRows / G;
   int log2_bs = 0;
   while ((1 << log2_bs) < a.block_size) ++log2_bs;
@@ -392,23 +420,25 @@ hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
   const int64_t total = static_cast<int64_t>(max_qt) * a.num_kv_heads * a.num_seqs;
   if (total > INT32_MAX) return hipErrorInvalidValue;
   dim3 grid(static_cast<uint32_t>(total));
-  hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(kThreads), 0, stream,
+  // an E4M3 cache holds K / k_scale: the score scale absorbs k_scale
+  const float scale_log2 = a.scale * (FP8 ? a.k_scale : 1.f) * kLog2e;
+  hipLaunchKernelGGL((prefill_kernel<D, G, FP8>), grid, dim3(kThreads), 0, stream,
                      static_cast<uint16_t*>(a.out), static_cast<const char*>(a.q), a.q_stride * 2,
                      static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache),
-                     a.k_stride * 2, a.v_stride * 2, a.cu_q,
+                     a.k_stride * KB, a.v_stride * KB, a.cu_q,
                      a.cu_k, a.block_tables, a.max_blocks, a.num_q_heads, a.num_kv_heads, log2_bs,
-                     a.scale * kLog2e, max_qt);
+                     scale_log2, max_qt, a.v_scale);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool FP8>
 hipError_t dispatch_prefill_group(const PrefillArgs& a, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_prefill_typed<D, 1>(a, stream);
-    case 2: return launch_prefill_typed<D, 2>(a, stream);
-    case 4: return launch_prefill_typed<D, 4>(a, stream);
-    case 8: return launch_prefill_typed<D, 8>(a, stream);
-    case 16: return launch_prefill_typed<D, 16>(a, stream);
+    case 1: return launch_prefill_typed<D, 1, FP8>(a, stream);
+    case 2: return launch_prefill_typed<D, 2, FP8>(a, stream);
+    case 4: return launch_prefill_typed<D, 4, FP8>(a, stream);
+    case 8: return launch_prefill_typed<D, 8, FP8>(a, stream);
+    case 16: return launch_prefill_typed<D, 16, FP8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -416,8 +446,12 @@ hipError_t dispatch_prefill_group(const PrefillArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-  return a.head_dim == 64 ? dispatch_prefill_group<64>(a, stream)
-                          : dispatch_prefill_group<128>(a, stream);
+  if (a.fp8) {
+    return a.head_dim == 64 ? dispatch_prefill_group<64, true>(a, stream)
+                            : dispatch_prefill_group<128, true>(a, stream);
+  }
+  return a.head_dim == 64 ? dispatch_prefill_group<64, false>(a, stream)
+                          : dispatch_prefill_group<128, false>(a, stream);
 }
 
 }  // namespace pa

@@ -9,6 +9,11 @@
 // thread. A 256-thread workgroup covers 256 / vectors-per-row tokens; rows
 // longer than 4 KiB are looped over. Address arithmetic is 64-bit: a pool can
 // exceed 2^31 bytes.
+//
+// E4M3 caches (FP8): the bf16 input rows are quantised on the way, each
+// element divided by the tensor's scale in fp32 and rounded to the nearest
+// E4M3 code (ties to even, saturating at +-448); a 16-byte input vector
+// becomes an 8-byte cache vector.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -18,11 +23,12 @@ namespace {
 
 constexpr int kThreads = 256;
 
+template <bool FP8>
 __global__ void __launch_bounds__(kThreads) store_kvcache_kernel(
     const char* __restrict__ key, int64_t key_stride, const char* __restrict__ value,
     int64_t value_stride, char* __restrict__ k_cache, char* __restrict__ v_cache,
     const int32_t* __restrict__ slot_mapping, int32_t num_tokens, int32_t vecs_per_row,
-    int32_t tokens_per_block, int32_t row_bytes) {
+    int32_t tokens_per_block, int32_t cache_row_bytes, float k_scale, float v_scale) {
   int32_t lane_token, c0, cstep;
   if (tokens_per_block > 0) {
     lane_token = static_cast<int32_t>(threadIdx.x) / vecs_per_row;
@@ -41,12 +47,17 @@ __global__ void __launch_bounds__(kThreads) store_kvcache_kernel(
   if (slot < 0) return;  // padding token: nothing to write
   const char* ksrc = key + static_cast<int64_t>(t) * key_stride;
   const char* vsrc = value + static_cast<int64_t>(t) * value_stride;
-  const int64_t dst = static_cast<int64_t>(slot) * row_bytes;
+  const int64_t dst = static_cast<int64_t>(slot) * cache_row_bytes;
   for (int32_t c = c0; c < vecs_per_row; c += cstep) {
     const Vec16 kv = load16(ksrc + c * 16);
     const Vec16 vv = load16(vsrc + c * 16);
-    store16(k_cache + dst + c * 16, kv);
-    store16(v_cache + dst + c * 16, vv);
+    if constexpr (FP8) {
+      store8(k_cache + dst + c * 8, quantize8(kv, k_scale));
+      store8(v_cache + dst + c * 8, quantize8(vv, v_scale));
+    } else {
+      store16(k_cache + dst + c * 16, kv);
+      store16(v_cache + dst + c * 16, vv);
+    }
   }
 }
 
@@ -58,11 +69,13 @@ hipError_t launch_store(const StoreArgs& a, hipStream_t stream) {
   const int32_t tpb = vecs <= kThreads ? kThreads / vecs : 0;
   const int32_t per = tpb > 0 ? tpb : 1;
   const int grid = (a.num_tokens + per - 1) / per;
-  hipLaunchKernelGGL(store_kvcache_kernel, dim3(grid), dim3(kThreads), 0, stream,
+  const int32_t cache_row_bytes = a.fp8 ? a.row_bytes / 2 : a.row_bytes;
+  auto kernel = a.fp8 ? store_kvcache_kernel<true> : store_kvcache_kernel<false>;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream,
                      static_cast<const char*>(a.key), a.key_stride_bytes,
                      static_cast<const char*>(a.value), a.value_stride_bytes,
                      static_cast<char*>(a.k_cache), static_cast<char*>(a.v_cache), a.slot_mapping,
-                     a.num_tokens, vecs, tpb, a.row_bytes);
+                     a.num_tokens, vecs, tpb, cache_row_bytes, a.k_scale, a.v_scale);
   return hipGetLastError();
 }
 

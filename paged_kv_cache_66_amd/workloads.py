@@ -26,9 +26,17 @@ The metadata rules follow the control-plane description on the pages:
 Random values are N(0, 1) drawn in fp32 and rounded to the storage dtype
 (round to nearest even for bf16). Rows of the pool that no sequence may read
 hold NaN, so any over-read shows up as a non-finite output.
+
+fp8 caches (``kv_dtype="fp8e4m3"``, next to bf16 queries and new rows) hold
+one-byte E4M3 codes with a per-tensor scale for K and V: the history rows are
+N(0, 1) / scale drawn in fp32, clamped to +-448 (torch's cast would turn the
+rare tail beyond it into NaN) and cast to torch.float8_e4m3fn, so the
+dequantised history again looks like N(0, 1); the NaN code 0x7F poisons the
+rows nobody may read.
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 from dataclasses import dataclass, field
 
@@ -143,7 +151,21 @@ def nan_value(dtype: str):
 
 
 def storage_np_dtype(dtype: str):
-    return np.uint16 if dtype == "bf16" else np.float32
+    return {"bf16": np.uint16, "f32": np.float32, "fp8e4m3": np.uint8}[dtype]
+
+
+FP8_NAN_CODE = np.uint8(0x7F)
+# per-tensor scale of the fp8 workloads: N(0, 1) history maps to codes of
+# N(0, 80^2), whose 5.6-sigma tail reaches the largest code (448)
+FP8_SCALE = 0.0125
+
+
+def fp8_codes(rng: np.random.Generator, shape, scale: float) -> np.ndarray:
+    """E4M3 codes of N(0, 1) / scale samples, clamped to +-448 (torch's
+    float8_e4m3fn cast)."""
+    import torch
+    x = np.clip(rng.standard_normal(shape, dtype=np.float32) / np.float32(scale), -448.0, 448.0)
+    return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
 def randn_storage(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
@@ -173,6 +195,9 @@ class DecodeWorkload:
     scale: float
     seed: int = 0
     note: str = ""
+    kv_dtype: str | None = None  # cache storage type when it differs from dtype ("fp8e4m3")
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def num_seqs(self) -> int:
@@ -184,14 +209,24 @@ class DecodeWorkload:
 
     @property
     def elem_bytes(self) -> int:
+        """Bytes per query / new-row / output element."""
         return 2 if self.dtype == "bf16" else 4
+
+    @property
+    def cache_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
+
+    @property
+    def kv_elem_bytes(self) -> int:
+        """Bytes per cache element."""
+        return 1 if self.cache_dtype == "fp8e4m3" else self.elem_bytes
 
     def readable_positions(self, b: int) -> int:
         """Rows that hold history before the step (positions 0 .. ctx-2)."""
         return max(int(self.context_lens[b]) - 1, 0)
 
     def kv_bytes_logical(self) -> int:
-        return int(self.context_lens.astype(np.int64).sum()) * 2 * self.num_kv_heads * self.head_dim * self.elem_bytes
+        return int(self.context_lens.astype(np.int64).sum()) * 2 * self.num_kv_heads * self.head_dim * self.kv_elem_bytes
 
     def kv_bytes_unique(self) -> int:
         """K/V bytes counted once per distinct (physical block, offset) row."""
@@ -207,7 +242,7 @@ class DecodeWorkload:
         best: dict[int, int] = {}
         for bid, hi in rows:
             best[bid] = max(best.get(bid, 0), hi)
-        return sum(best.values()) * 2 * self.num_kv_heads * self.head_dim * self.elem_bytes
+        return sum(best.values()) * 2 * self.num_kv_heads * self.head_dim * self.kv_elem_bytes
 
     def algorithmic_bytes(self, unique: bool = False) -> int:
         """Bytes the decode step must move: K/V rows once per kv head, q in,
@@ -222,8 +257,10 @@ class DecodeWorkload:
         return 4 * ctx * self.num_q_heads * self.head_dim
 
     def store_bytes(self) -> int:
+        """K and V rows read from the inputs and written to the caches."""
         t = int((self.slot_mapping >= 0).sum())
-        return t * 2 * 2 * self.num_kv_heads * self.head_dim * self.elem_bytes + 4 * len(self.slot_mapping)
+        return (t * 2 * self.num_kv_heads * self.head_dim * (self.elem_bytes + self.kv_elem_bytes)
+                + 4 * len(self.slot_mapping))
 
 
 @dataclass
@@ -252,6 +289,9 @@ class PrefillWorkload:
     seed: int = 0
     shared_groups: list = field(default_factory=list)
     note: str = ""
+    kv_dtype: str | None = None
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def num_seqs(self) -> int:
@@ -267,7 +307,17 @@ class PrefillWorkload:
 
     @property
     def elem_bytes(self) -> int:
+        """Bytes per query / new-row / output element."""
         return 2 if self.dtype == "bf16" else 4
+
+    @property
+    def cache_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
+
+    @property
+    def kv_elem_bytes(self) -> int:
+        """Bytes per cache element."""
+        return 1 if self.cache_dtype == "fp8e4m3" else self.elem_bytes
 
     def flops(self) -> int:
         """QK^T + PV multiply-adds (2 flops each) over unmasked pairs only."""
@@ -278,8 +328,10 @@ class PrefillWorkload:
         return 4 * self.head_dim * self.num_q_heads * tot
 
     def store_bytes(self) -> int:
+        """K and V rows read from the inputs and written to the caches."""
         t = int((self.slot_mapping >= 0).sum())
-        return t * 2 * 2 * self.num_kv_heads * self.head_dim * self.elem_bytes + 4 * len(self.slot_mapping)
+        return (t * 2 * self.num_kv_heads * self.head_dim * (self.elem_bytes + self.kv_elem_bytes)
+                + 4 * len(self.slot_mapping))
 
 
 # ---------------------------------------------------------------------------
@@ -452,7 +504,22 @@ DECODE_CONFIGS = {
     "8b-decode-bs256": lambda seed=0: large_batch_decode(256, seed),
     "long-context-decode": long_context_decode,
 }
-PREFILL_CONFIGS = {"chunked-prefill": chunked_prefill}
+
+
+def with_fp8_cache(w, k_scale: float = FP8_SCALE, v_scale: float = FP8_SCALE):
+    """The same workload over E4M3 caches (bf16 queries and new rows)."""
+    assert w.dtype == "bf16", "fp8 caches pair with bf16 queries"
+    return dataclasses.replace(w, name=w.name + "-fp8", kv_dtype="fp8e4m3", k_scale=k_scale,
+                               v_scale=v_scale)
+
+
+DECODE_CONFIGS.update({
+    "qwen3-0.6b-decode-fp8": lambda seed=0: with_fp8_cache(qwen3_0p6b_decode(seed)),
+    "long-context-decode-fp8": lambda seed=0: with_fp8_cache(long_context_decode(seed)),
+})
+
+PREFILL_CONFIGS = {"chunked-prefill": chunked_prefill,
+                   "chunked-prefill-fp8": lambda seed=0: with_fp8_cache(chunked_prefill(seed))}
 
 
 # ---------------------------------------------------------------------------
@@ -501,11 +568,15 @@ def make_host_tensors(w, seed: int | None = None) -> dict:
     produce them."""
     rng = np.random.default_rng(w.seed * 7919 + 17 if seed is None else seed)
     h, hq, d, bs = w.num_kv_heads, w.num_q_heads, w.head_dim, w.block_size
-    nanv = nan_value(w.dtype)
-    k_cache = np.full((w.num_blocks, bs, h, d), nanv, dtype=storage_np_dtype(w.dtype))
+    fp8 = w.cache_dtype == "fp8e4m3"
+    nanv = FP8_NAN_CODE if fp8 else nan_value(w.dtype)
+    k_cache = np.full((w.num_blocks, bs, h, d), nanv, dtype=storage_np_dtype(w.cache_dtype))
     v_cache = np.full_like(k_cache, nanv)
     for bid, rows in sorted(readable_rows(w).items()):
-        if rows:
+        if rows and fp8:
+            k_cache[bid, :rows] = fp8_codes(rng, (rows, h, d), w.k_scale)
+            v_cache[bid, :rows] = fp8_codes(rng, (rows, h, d), w.v_scale)
+        elif rows:
             k_cache[bid, :rows] = randn_storage(rng, (rows, h, d), w.dtype)
             v_cache[bid, :rows] = randn_storage(rng, (rows, h, d), w.dtype)
     t = w.num_seqs if isinstance(w, DecodeWorkload) else w.total_q
@@ -521,23 +592,28 @@ def make_device_tensors(w, device="cuda", seed: int | None = None, chunk_blocks:
     seeded torch generator so multi-GB pools never pass through the host.
 
     Same layout as :func:`make_host_tensors`; bf16 tensors have dtype
-    torch.bfloat16, fp32 ones torch.float32."""
+    torch.bfloat16, fp32 ones torch.float32, fp8 caches torch.uint8."""
     import torch
 
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    fp8 = w.cache_dtype == "fp8e4m3"
     g = torch.Generator(device=device)
     g.manual_seed(w.seed * 7919 + 17 if seed is None else seed)
     h, hq, d, bs = w.num_kv_heads, w.num_q_heads, w.head_dim, w.block_size
     n = w.num_blocks
-    k_cache = torch.empty((n, bs, h, d), dtype=tdt, device=device)
+    k_cache = torch.empty((n, bs, h, d), dtype=torch.uint8 if fp8 else tdt, device=device)
     v_cache = torch.empty_like(k_cache)
     row = bs * h * d
     step = chunk_blocks or max(1, (1 << 28) // row)
-    for cache in (k_cache, v_cache):
+    for cache, sc in ((k_cache, w.k_scale), (v_cache, w.v_scale)):
         flat = cache.view(n, row)
         for s in range(0, n, step):
             e = min(n, s + step)
-            flat[s:e].copy_(torch.randn((e - s, row), generator=g, device=device, dtype=torch.float32))
+            x = torch.randn((e - s, row), generator=g, device=device, dtype=torch.float32)
+            if fp8:
+                flat[s:e].copy_((x / sc).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8))
+            else:
+                flat[s:e].copy_(x)
     # poison every row that holds no history
     rr = readable_rows(w)
     keep = np.zeros(n, dtype=bool)
@@ -550,7 +626,7 @@ def make_device_tensors(w, device="cuda", seed: int | None = None, chunk_blocks:
             partial_ids.append(bid)
             partial_rows.append(rows)
     dead = torch.from_numpy(np.nonzero(~keep)[0]).to(device)
-    nanv = float("nan")
+    nanv = int(FP8_NAN_CODE) if fp8 else float("nan")
     for cache in (k_cache, v_cache):
         if dead.numel():
             cache.index_fill_(0, dead, nanv)

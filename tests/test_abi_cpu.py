@@ -26,7 +26,8 @@ def test_exports_every_header_symbol(lib):
     names = binding.header_symbols()
     assert set(names) == {"pa_status_string", "pa_version", "pa_store_kvcache",
                           "pa_decode_workspace_size", "pa_decode", "pa_store_decode",
-                          "pa_prefill_varlen"}
+                          "pa_prefill_varlen", "pa_store_kvcache_fp8", "pa_decode_fp8",
+                          "pa_store_decode_fp8", "pa_prefill_varlen_fp8"}
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -162,6 +163,84 @@ def test_prefill_validation(lib):
     assert prefill(lib, **{**packed, "ks": 260}) == ALIGN
     assert prefill(lib, **{**packed, "k": A + 8}) == ALIGN
     assert prefill(lib, **{**packed, "ks": 1 << 26}) == SHAPE
+
+
+# ---- fp8 (E4M3) cache entry points: bf16 rows, one-byte caches, two scales ----
+
+def store_fp8(lib, **kw):
+    a = dict(key=A, ks=128, value=A, vs=128, kc=A, vc=A, slots=A, t=4, n=32, bs=16, hkv=2, d=64,
+             kscale=0.02, vscale=0.03, dtype=BF16)
+    a.update(kw)
+    return lib.pa_store_kvcache_fp8(a["key"], a["ks"], a["value"], a["vs"], a["kc"], a["vc"], a["slots"],
+                                    a["t"], a["n"], a["bs"], a["hkv"], a["d"], a["kscale"], a["vscale"],
+                                    a["dtype"], None)
+
+
+def test_store_fp8_validation(lib):
+    assert store_fp8(lib, t=0, key=None, value=None, slots=None) == OK
+    assert store_fp8(lib, dtype=F32) == UNSUP       # bf16 rows only
+    assert store_fp8(lib, kscale=0.0) == SHAPE
+    assert store_fp8(lib, vscale=float("inf")) == SHAPE
+    assert store_fp8(lib, kscale=-1.0) == SHAPE
+    assert store_fp8(lib, kc=None) == NULL
+    assert store_fp8(lib, slots=None) == NULL
+    assert store_fp8(lib, d=96) == UNSUP
+    assert store_fp8(lib, ks=100) == SHAPE
+    assert store_fp8(lib, ks=132) == ALIGN          # 264-byte bf16 rows
+    assert store_fp8(lib, vc=A + 8) == ALIGN
+
+
+def decode_fp8(lib, fused=False, **kw):
+    a = dict(out=A, q=A, qs=256, key=A, ks=128, value=A, vs=128, slots=A, kc=A, vc=A, bt=A, w=4, ctx=A,
+             b=4, hq=4, hkv=2, d=64, bs=16, n=32, scale=0.125, kscale=0.02, vscale=0.03, part=0,
+             dtype=BF16, ws=None, wsn=0)
+    a.update(kw)
+    if fused:
+        return lib.pa_store_decode_fp8(a["out"], a["q"], a["qs"], a["key"], a["ks"], a["value"], a["vs"],
+                                       a["slots"], a["kc"], a["vc"], a["bt"], a["w"], a["ctx"], a["b"],
+                                       a["hq"], a["hkv"], a["d"], a["bs"], a["n"], a["scale"], a["kscale"],
+                                       a["vscale"], a["part"], a["dtype"], a["ws"], a["wsn"], None)
+    return lib.pa_decode_fp8(a["out"], a["q"], a["qs"], a["kc"], a["vc"], a["bt"], a["w"], a["ctx"], a["b"],
+                             a["hq"], a["hkv"], a["d"], a["bs"], a["n"], a["scale"], a["kscale"],
+                             a["vscale"], a["part"], a["dtype"], a["ws"], a["wsn"], None)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_decode_fp8_validation(lib, fused):
+    assert decode_fp8(lib, fused, b=0, out=None, q=None) == OK
+    assert decode_fp8(lib, fused, dtype=F32) == UNSUP
+    assert decode_fp8(lib, fused, kscale=0.0) == SHAPE
+    assert decode_fp8(lib, fused, vscale=float("nan")) == SHAPE
+    assert decode_fp8(lib, fused, scale=0.0) == SHAPE
+    assert decode_fp8(lib, fused, out=None) == NULL
+    assert decode_fp8(lib, fused, hq=6, hkv=2) == UNSUP
+    assert decode_fp8(lib, fused, qs=100) == SHAPE
+    assert decode_fp8(lib, fused, w=128) == WS
+    if fused:
+        assert decode_fp8(lib, fused, key=None) == NULL
+        assert decode_fp8(lib, fused, vs=130) == ALIGN
+
+
+def prefill_fp8(lib, **kw):
+    a = dict(out=A, q=A, qs=512, tq=8, kc=A, vc=A, cuq=A, cuk=A, mq=8, mk=8, bt=A, w=4, b=1,
+             hq=4, hkv=2, d=128, bs=16, n=32, scale=0.1, kscale=0.02, vscale=0.03, dtype=BF16)
+    a.update(kw)
+    return lib.pa_prefill_varlen_fp8(a["out"], a["q"], a["qs"], a["tq"], a["kc"], a["vc"], a["cuq"],
+                                     a["cuk"], a["mq"], a["mk"], a["bt"], a["w"], a["b"], a["hq"],
+                                     a["hkv"], a["d"], a["bs"], a["n"], a["scale"], a["kscale"],
+                                     a["vscale"], a["dtype"], None)
+
+
+def test_prefill_fp8_validation(lib):
+    assert prefill_fp8(lib, b=0) == OK
+    assert prefill_fp8(lib, bt=None) == NULL    # fp8 data lives only in the paged caches
+    assert prefill_fp8(lib, dtype=F32) == UNSUP
+    assert prefill_fp8(lib, kscale=0.0) == SHAPE
+    assert prefill_fp8(lib, vscale=-2.0) == SHAPE
+    assert prefill_fp8(lib, cuq=None) == NULL
+    assert prefill_fp8(lib, d=32) == UNSUP
+    assert prefill_fp8(lib, bs=24) == UNSUP
+    assert prefill_fp8(lib, kc=A + 8) == ALIGN
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
