@@ -13,8 +13,9 @@ every step reads its KV cold, as a layer's KV would be in a real model step
 Also measured in the same run (unless --quick): the chunked varlen prefill
 workload (16384 query tokens over 24 sequences with shared cached prefixes:
 store + pa_prefill_varlen; the metric's second half), the 8B-shaped
-large-batch decode at block sizes 16 and 256, and the 131072-token
-long-context split-K decode.
+large-batch decode at block sizes 16 and 256, the 131072-token
+long-context split-K decode, and the headline decode, the long-context
+decode and the chunked prefill again over fp8 (E4M3) caches.
 
 Prints one JSON line. `value` = decode algorithmic bytes per step / step
 time. `roofline` describes the decode call (the dominant kernel) timed with
@@ -105,12 +106,31 @@ def run_decode(torch, binding, wl, w, steps, warmup, flush, scratch, partition=0
                                             w.block_size, w.max_blocks_per_seq, partition)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
 
+    fp8 = w.cache_dtype == "fp8e4m3"
+
     def step():
-        binding.pa_store_kvcache(t["k"], t["v"], t["k_cache"], t["v_cache"], slots)
+        if fp8:
+            binding.pa_store_kvcache_fp8(t["k"], t["v"], t["k_cache"], t["v_cache"], slots, w.k_scale,
+                                         w.v_scale)
+        else:
+            binding.pa_store_kvcache(t["k"], t["v"], t["k_cache"], t["v_cache"], slots)
 
     def dec():
-        binding.pa_decode(t["q"], t["k_cache"], t["v_cache"], tables, ctx, w.scale, out=out,
-                          workspace=ws, partition_size=partition)
+        if fp8:
+            binding.pa_decode_fp8(t["q"], t["k_cache"], t["v_cache"], tables, ctx, w.scale, w.k_scale,
+                                  w.v_scale, out=out, workspace=ws, partition_size=partition)
+        else:
+            binding.pa_decode(t["q"], t["k_cache"], t["v_cache"], tables, ctx, w.scale, out=out,
+                              workspace=ws, partition_size=partition)
+
+    def fused():
+        if fp8:
+            binding.pa_store_decode_fp8(t["q"], t["k"], t["v"], slots, t["k_cache"], t["v_cache"], tables,
+                                        ctx, w.scale, w.k_scale, w.v_scale, out=out, workspace=ws,
+                                        partition_size=partition)
+        else:
+            binding.pa_store_decode(t["q"], t["k"], t["v"], slots, t["k_cache"], t["v_cache"], tables, ctx,
+                                    w.scale, out=out, workspace=ws, partition_size=partition)
 
     for _ in range(warmup):
         step()
@@ -139,8 +159,7 @@ def run_decode(torch, binding, wl, w, steps, warmup, flush, scratch, partition=0
         if flush:
             flush_caches(scratch)
         ftimer.rec(s, 0)
-        binding.pa_store_decode(t["q"], t["k"], t["v"], slots, t["k_cache"], t["v_cache"], tables, ctx,
-                                w.scale, out=out, workspace=ws, partition_size=partition)
+        fused()
         ftimer.rec(s, 1)
     torch.cuda.synchronize()
     fused_ms = sum(ftimer.span(0, 1)) / steps
@@ -170,13 +189,22 @@ def run_prefill(torch, binding, wl, w, steps, warmup, flush, scratch):
     cuk = torch.from_numpy(w.cu_seqlens_k).cuda()
     tables = torch.from_numpy(w.block_tables).cuda()
     out = torch.empty((w.total_q, w.num_q_heads, w.head_dim), dtype=t["q"].dtype, device="cuda")
+    fp8 = w.cache_dtype == "fp8e4m3"
 
     def store():
-        binding.pa_store_kvcache(t["k"], t["v"], t["k_cache"], t["v_cache"], slots)
+        if fp8:
+            binding.pa_store_kvcache_fp8(t["k"], t["v"], t["k_cache"], t["v_cache"], slots, w.k_scale,
+                                         w.v_scale)
+        else:
+            binding.pa_store_kvcache(t["k"], t["v"], t["k_cache"], t["v_cache"], slots)
 
     def pre():
-        binding.pa_prefill_varlen(t["q"], t["k_cache"], t["v_cache"], cuq, cuk, w.max_seqlen_q,
-                                  w.max_seqlen_k, tables, w.scale, out=out)
+        if fp8:
+            binding.pa_prefill_varlen_fp8(t["q"], t["k_cache"], t["v_cache"], cuq, cuk, w.max_seqlen_q,
+                                          w.max_seqlen_k, tables, w.scale, w.k_scale, w.v_scale, out=out)
+        else:
+            binding.pa_prefill_varlen(t["q"], t["k_cache"], t["v_cache"], cuq, cuk, w.max_seqlen_q,
+                                      w.max_seqlen_k, tables, w.scale, out=out)
 
     for _ in range(warmup):
         store()
@@ -343,7 +371,9 @@ def main():
         ks = max(5, args.steps // 3)
         for name, mk in [("8b-decode-bs16", lambda: wl.large_batch_decode(16, 0)),
                          ("8b-decode-bs256", lambda: wl.large_batch_decode(256, 0)),
-                         ("long-context-decode", lambda: wl.long_context_decode(0))]:
+                         ("long-context-decode", lambda: wl.long_context_decode(0)),
+                         ("qwen3-0.6b-decode-fp8", lambda: wl.DECODE_CONFIGS["qwen3-0.6b-decode-fp8"](0)),
+                         ("long-context-decode-fp8", lambda: wl.DECODE_CONFIGS["long-context-decode-fp8"](0))]:
             log(f"[bench] {name}")
             r, _ = run_decode(torch, binding, wl, mk(), ks, 2, flush, scratch, args.partition, name)
             torch.cuda.empty_cache()
@@ -357,6 +387,11 @@ def main():
         torch.cuda.empty_cache()
         secondary["chunked-prefill"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in p.items()}
         log(f"[bench] prefill {p['prefill_ms']:.3f} ms, {p['prefill_TFLOPs']:.1f} TFLOP/s")
+        log("[bench] chunked-prefill-fp8")
+        p = run_prefill(torch, binding, wl, wl.PREFILL_CONFIGS["chunked-prefill-fp8"](0), ks, 2, flush, scratch)
+        torch.cuda.empty_cache()
+        secondary["chunked-prefill-fp8"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in p.items()}
+        log(f"[bench] prefill fp8 {p['prefill_ms']:.3f} ms, {p['prefill_TFLOPs']:.1f} TFLOP/s")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -208,9 +208,12 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   constexpr int TPW = 64 / LPT;      // rows per wave per load
   constexpr int STEP = kWaves * TPW; // rows per workgroup per load
 
+  // fused: the new row's K and V head slices, in cache format, come first
+  constexpr int kNewWords = FUSED ? 2 * D * EB / 4 : 0;
   extern __shared__ float lds[];
-  float* s_score = lds;                                   // [partition][G]
-  float* s_max = lds + score_words;                       // [G]
+  char* s_new = reinterpret_cast<char*>(lds);             // [2][D] cache elements
+  float* s_score = lds + kNewWords;                       // [partition][G]
+  float* s_max = s_score + score_words;                   // [G]
   float* s_sum = s_max + G;                               // [G]
   int32_t* s_ids = reinterpret_cast<int32_t*>(s_sum + G);  // block ids of the partition
 
@@ -256,6 +259,41 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   const int32_t* table = block_tables + static_cast<int64_t>(b) * max_blocks;
   for (int i = tid; i < nblk; i += kThreads) s_ids[i] = table[jb0 + i];
 
+  // The step's new row (fused scatter). When this partition holds position
+  // n - 1 and the slot is >= 0, new_tl = n - 1 - t0 = ntok - 1: the last row
+  // of the partition. Its head slices are written to the cache slot
+  // (quantised first for an E4M3 cache) and to LDS, and nothing in this
+  // launch reads them back from the cache: the loops below stop one row
+  // short, and the row's score and weighted value are taken from LDS after
+  // them. Every lane takes its rows in increasing order, so handling the last
+  // row after the loop keeps the summation order of pa_decode.
+  const int row_bytes_h = D * EB;  // one kv head's slice of a cache row
+  int new_tl = -1;
+  if constexpr (FUSED) {
+    const int slot = slot_mapping[b];
+    if (slot >= 0 && n - 1 >= t0 && n - 1 < t1) {
+      new_tl = n - 1 - t0;
+      constexpr int kVecs = D / EPV;  // lane vectors per head slice
+      if (tid < 2 * kVecs) {
+        const bool is_v = tid >= kVecs;
+        const int c = is_v ? tid - kVecs : tid;
+        const char* row = is_v ? new_v + static_cast<int64_t>(b) * new_v_stride_bytes
+                               : new_k + static_cast<int64_t>(b) * new_k_stride_bytes;
+        const Vec16 x = load16(row + (static_cast<int64_t>(g) * D + c * EPV) * QB);
+        Vec y;
+        if constexpr (kFp8) {
+          y = quantize8(x, is_v ? v_scale : k_scale);
+        } else {
+          y = x;
+        }
+        const int64_t dst = static_cast<int64_t>(slot) * static_cast<int64_t>(num_kv_heads) * row_bytes_h +
+                            static_cast<int64_t>(g) * row_bytes_h + c * VB;
+        *reinterpret_cast<Vec*>((is_v ? v_cache : k_cache) + dst) = y;
+        *reinterpret_cast<Vec*>(s_new + (is_v ? row_bytes_h : 0) + c * VB) = y;
+      }
+    }
+  }
+
   const int grp1 = lane / LPT1;
   const int li1 = lane % LPT1;
   QSlice<T> qs[G];
@@ -282,59 +320,20 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
     return static_cast<uint64_t>((blk << log2_bs) + (pos & bs_mask)) * row_bytes;
   };
 
-  // The step's new row (fused scatter): local index in this partition, or -1
-  // when it is not here or not stored. Its head slice is written to the cache
-  // slot once, here, and nothing in this launch reads it back from there:
-  // 16-bit and fp32 caches take the row from the inputs by selecting the
-  // address per row; an E4M3 cache needs the quantised codes, so every lane
-  // quantises its own slices of the new row into registers and selects the
-  // data instead.
-  int new_tl = -1;
-  const char* nk_row = nullptr;
-  const char* nv_row = nullptr;
-  Vec nk0{}, nk1{}, nv{};
-  if constexpr (FUSED) {
-    const int slot = slot_mapping[b];
-    if (slot >= 0 && n - 1 >= t0 && n - 1 < t1) {
-      new_tl = n - 1 - t0;
-      nk_row = new_k + static_cast<int64_t>(b) * new_k_stride_bytes + static_cast<int64_t>(g) * D * QB;
-      nv_row = new_v + static_cast<int64_t>(b) * new_v_stride_bytes + static_cast<int64_t>(g) * D * QB;
-      const int64_t dst = static_cast<int64_t>(slot) * static_cast<int64_t>(row_bytes) +
-                          static_cast<int64_t>(g) * D * EB;
-      constexpr int kVecs = D * QB / 16;  // 16-byte input vectors per head slice
-      if constexpr (kFp8) {
-        if (tid < kVecs) store8(k_cache + dst + tid * 8, quantize8(load16(nk_row + tid * 16), k_scale));
-        else if (tid < 2 * kVecs)
-          store8(v_cache + dst + (tid - kVecs) * 8, quantize8(load16(nv_row + (tid - kVecs) * 16), v_scale));
-        nk0 = quantize8(load16(nk_row + li1 * 16), k_scale);
-        nk1 = quantize8(load16(nk_row + (LPT1 + li1) * 16), k_scale);
-        nv = quantize8(load16(nv_row + li * 16), v_scale);
-      } else {
-        if (tid < kVecs) store16(k_cache + dst + tid * 16, load16(nk_row + tid * 16));
-        else if (tid < 2 * kVecs) store16(v_cache + dst + (tid - kVecs) * 16, load16(nv_row + (tid - kVecs) * 16));
-      }
-    }
-  }
+  const int nloop = new_tl >= 0 ? ntok - 1 : ntok;  // rows read from the cache
 
   // phase 1: raw scores q . k (the scale is applied once per score in phase 2)
   const char* kbase1 = k_cache + static_cast<int64_t>(g) * D * EB + li1 * VB;
   const int my_row1 = wave * TPW1 + grp1;
-  for (int base = 0; base < ntok; base += STEP1 * kUnroll) {
+  for (int base = 0; base < nloop; base += STEP1 * kUnroll) {
     Vec k0[kUnroll], k1[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int tl = base + u * STEP1 + my_row1;
-      if (tl < ntok) {
+      if (tl < nloop) {
         const char* r = kbase1 + row_off(tl);
-        if constexpr (FUSED && !kFp8) r = tl == new_tl ? nk_row + li1 * 16 : r;
         k0[u] = E::load_nt(r);
         k1[u] = E::load_nt(r + LPT1 * VB);
-        if constexpr (FUSED && kFp8) {
-          if (tl == new_tl) {
-            k0[u] = nk0;
-            k1[u] = nk1;
-          }
-        }
       } else {
         k0[u] = Vec{};
         k1[u] = Vec{};
@@ -346,9 +345,22 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
       float sc[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) sc[h] = group_sum<LPT1>(qs[h].dot(k0[u], k1[u]));
-      if (li1 == 0 && tl < ntok) {
+      if (li1 == 0 && tl < nloop) {
 #pragma unroll
         for (int h = 0; h < G; ++h) s_score[tl * G + h] = sc[h];
+      }
+    }
+  }
+  if constexpr (FUSED) {
+    if (new_tl >= 0) {  // uniform: every lane joins the row-group sums
+      const Vec nk0 = *reinterpret_cast<const Vec*>(s_new + li1 * VB);
+      const Vec nk1 = *reinterpret_cast<const Vec*>(s_new + (LPT1 + li1) * VB);
+      float sc[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) sc[h] = group_sum<LPT1>(qs[h].dot(nk0, nk1));
+      if (li1 == 0 && my_row1 == new_tl % STEP1) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) s_score[new_tl * G + h] = sc[h];
       }
     }
   }
@@ -382,18 +394,13 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 #pragma unroll
     for (int e = 0; e < EPV; ++e) acc[h][e] = 0.f;
 
-  for (int base = 0; base < ntok; base += STEP * kUnroll) {
+  for (int base = 0; base < nloop; base += STEP * kUnroll) {
     Vec vv[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int tl = base + u * STEP + my_row;
-      if (tl < ntok) {
-        const char* r = vbase + row_off(tl);
-        if constexpr (FUSED && !kFp8) r = tl == new_tl ? nv_row + li * 16 : r;
-        vv[u] = E::load_nt(r);
-        if constexpr (FUSED && kFp8) {
-          if (tl == new_tl) vv[u] = nv;
-        }
+      if (tl < nloop) {
+        vv[u] = E::load_nt(vbase + row_off(tl));
       } else {
         vv[u] = Vec{};
       }
@@ -401,7 +408,7 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int tl = base + u * STEP + my_row;
-      if (tl < ntok) {
+      if (tl < nloop) {
         float vf[EPV];
         E::to_f32(vv[u], vf);
 #pragma unroll
@@ -410,6 +417,19 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 #pragma unroll
           for (int e = 0; e < EPV; ++e) acc[h][e] = fmaf(w, vf[e], acc[h][e]);
         }
+      }
+    }
+  }
+  if constexpr (FUSED) {
+    // the new row is this lane's last row, so it is added last, as in pa_decode
+    if (new_tl >= 0 && my_row == new_tl % STEP) {
+      float vf[EPV];
+      E::to_f32(*reinterpret_cast<const Vec*>(s_new + row_bytes_h + li * VB), vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float w = s_score[new_tl * G + h];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[h][e] = fmaf(w, vf[e], acc[h][e]);
       }
     }
   }
@@ -425,7 +445,7 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
       acc[h][e] = v;
     }
   __syncthreads();  // all reads of p are done; the score area becomes the reduction area
-  float* s_red = lds;  // [kWaves][G][D]
+  float* s_red = s_score;  // [kWaves][G][D]
   if (grp == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -529,7 +549,8 @@ hipError_t launch_decode_typed(const DecodeArgs& a, hipStream_t stream) {
   while ((1 << log2_bs) < a.block_size) ++log2_bs;
   const int score_words = G * (a.partition > 4 * D ? a.partition : 4 * D);
   const int max_ids = a.partition / (a.block_size < a.partition ? a.block_size : a.partition) + 2;
-  const size_t lds = static_cast<size_t>(score_words + 2 * G + max_ids) * 4;
+  const int new_words = FUSED ? 2 * D * Elem<T>::kBytes / 4 : 0;  // the fused new row
+  const size_t lds = static_cast<size_t>(new_words + score_words + 2 * G + max_ids) * 4;
   // an E4M3 cache holds K / k_scale: the score scale absorbs k_scale
   const float scale_log2 = a.scale * (Elem<T>::kBytes == 1 ? a.k_scale : 1.f) * kLog2e;
   dim3 grid(a.num_partitions * a.num_kv_heads * a.num_seqs);

@@ -7,10 +7,12 @@ Operations:
   decode <workload>   pa_store_kvcache of the new tokens + pa_decode, inputs
                       resident, a 1 GiB read between calls (cold caches);
   store_decode <workload>  the same step as one pa_store_decode launch;
-  prefill             pa_store_kvcache + pa_prefill_varlen on chunked-prefill;
+  prefill [workload]  pa_store_kvcache + pa_prefill_varlen on chunked-prefill
+                      (or chunked-prefill-fp8: the _fp8 entry points);
   copy                a 1 GiB device-to-device copy (counter calibration:
                       reads 1 GiB, writes 1 GiB).
-Workloads are the seeded synthetic ones of ``workloads.py``.
+Workloads are the seeded synthetic ones of ``workloads.py``; a workload over
+fp8 caches (name ending in -fp8) runs the *_fp8 entry points.
 """
 from __future__ import annotations
 
@@ -43,7 +45,9 @@ def main(argv=None):
         for _ in range(args.reps):
             dst.copy_(scratch)
     elif args.op == "prefill":
-        w = wl.chunked_prefill(0)
+        name = args.workload if args.workload in wl.PREFILL_CONFIGS else "chunked-prefill"
+        w = wl.PREFILL_CONFIGS[name](0)
+        fp8 = w.cache_dtype == "fp8e4m3"
         t = wl.make_device_tensors(w)
         slots = torch.from_numpy(w.slot_mapping).cuda()
         cuq = torch.from_numpy(w.cu_seqlens_q).cuda()
@@ -52,11 +56,18 @@ def main(argv=None):
         out = torch.empty((w.total_q, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
         for _ in range(args.reps):
             scratch.amax()
+            if fp8:
+                binding.pa_store_kvcache_fp8(t["k"], t["v"], t["k_cache"], t["v_cache"], slots, w.k_scale,
+                                             w.v_scale)
+                binding.pa_prefill_varlen_fp8(t["q"], t["k_cache"], t["v_cache"], cuq, cuk, w.max_seqlen_q,
+                                              w.max_seqlen_k, tables, w.scale, w.k_scale, w.v_scale, out=out)
+                continue
             binding.pa_store_kvcache(t["k"], t["v"], t["k_cache"], t["v_cache"], slots)
             binding.pa_prefill_varlen(t["q"], t["k_cache"], t["v_cache"], cuq, cuk, w.max_seqlen_q,
                                       w.max_seqlen_k, tables, w.scale, out=out)
     else:
         w = wl.DECODE_CONFIGS[args.workload](0)
+        fp8 = w.cache_dtype == "fp8e4m3"
         t = wl.make_device_tensors(w)
         slots = torch.from_numpy(w.slot_mapping).cuda()
         tables = torch.from_numpy(w.block_tables).cuda()
@@ -64,15 +75,24 @@ def main(argv=None):
         out = torch.empty_like(t["q"].contiguous())
         for _ in range(args.reps):
             scratch.amax()
-            if args.op == "store_decode":
+            if args.op == "store_decode" and fp8:
+                binding.pa_store_decode_fp8(t["q"], t["k"], t["v"], slots, t["k_cache"], t["v_cache"],
+                                            tables, ctx, w.scale, w.k_scale, w.v_scale, out=out,
+                                            partition_size=args.partition)
+            elif args.op == "store_decode":
                 binding.pa_store_decode(t["q"], t["k"], t["v"], slots, t["k_cache"], t["v_cache"], tables,
                                         ctx, w.scale, out=out, partition_size=args.partition)
-                continue
-            binding.pa_store_kvcache(t["k"], t["v"], t["k_cache"], t["v_cache"], slots)
-            binding.pa_decode(t["q"], t["k_cache"], t["v_cache"], tables, ctx, w.scale, out=out,
-                              partition_size=args.partition)
+            elif fp8:
+                binding.pa_store_kvcache_fp8(t["k"], t["v"], t["k_cache"], t["v_cache"], slots, w.k_scale,
+                                             w.v_scale)
+                binding.pa_decode_fp8(t["q"], t["k_cache"], t["v_cache"], tables, ctx, w.scale, w.k_scale,
+                                      w.v_scale, out=out, partition_size=args.partition)
+            else:
+                binding.pa_store_kvcache(t["k"], t["v"], t["k_cache"], t["v_cache"], slots)
+                binding.pa_decode(t["q"], t["k_cache"], t["v_cache"], tables, ctx, w.scale, out=out,
+                                  partition_size=args.partition)
     torch.cuda.synchronize()
-    print(f"profile_ops {args.op} {args.workload if 'decode' in args.op else ''} done", flush=True)
+    print(f"profile_ops {args.op} {args.workload if args.op != 'copy' else ''} done", flush=True)
 
 
 if __name__ == "__main__":
