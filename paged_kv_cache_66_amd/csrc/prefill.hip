@@ -20,14 +20,17 @@
 //   softmax statistics then need only two cross-lane steps per column;
 // * O^T = V^T P^T: the B operand P^T is assembled in registers straight from
 //   the score accumulators (the contraction index is permuted identically on
-//   both operands), and V is written to LDS transposed ([d][key]) so the A
-//   operand is two 8-byte LDS reads;
+//   both operands); V stays in LDS in its natural [key][d] layout and the A
+//   operand V^T comes from two transposing LDS reads (ds_read_b64_tr_b16:
+//   each lane receives one head_dim column over four consecutive keys);
 // * online softmax in the log2 domain: the running max is taken on raw
 //   scores and the scale is folded into the one FMA that feeds exp2; only the
 //   tiles that cross the causal diagonal or the end of the keys are masked;
 // * K/V tiles are double-buffered in LDS: the next tile's rows travel from
 //   HBM into registers while the current tile is multiplied, and one barrier
-//   per tile separates the buffer writes from the reads.
+//   per tile separates the buffer writes from the reads. Tiles that lie
+//   wholly inside the keys (all but the last) are fetched without per-row
+//   bounds checks.
 // * E4M3 caches (FP8): tiles travel as one-byte codes and are widened to bf16
 //   (exactly) on their way into LDS; k_scale joins the softmax scale and
 //   v_scale the final normalisation.
@@ -40,6 +43,8 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int kWavesPerGroup = 4;
 constexpr int kThreads = 64 * kWavesPerGroup;
@@ -72,9 +77,13 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          c, false);
 }
 
-__device__ __forceinline__ uint32_t half16(const Vec16& v, int j) {
-  const uint32_t w = v.w[j >> 1];
-  return (j & 1) ? (w >> 16) : (w & 0xffffu);
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// i % 4 of the 8-byte chunks addressed by lanes i / 4 + 4k (k = 0..3). With
+// lane m addressing row m / 4, columns 4 (m % 4) .. + 3 of a [row][col] tile,
+// lane i gets column i of rows 0..3.
+__device__ __forceinline__ s16x4_t ds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<lds_s16x4_t*>(reinterpret_cast<uintptr_t>(p)));
 }
 
 // Eight key / value elements as the tile loads carry them (bf16, or E4M3
@@ -109,15 +118,14 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   constexpr int KS = D / 32;       // MFMA k-steps over head_dim
   constexpr int DT = D / 16;       // 16-wide head_dim tiles of the output
   constexpr int KPITCH = D + 8;    // bf16 per K row in LDS (padding spreads banks)
-  constexpr int VPITCH = kKeys + 4;  // bf16 per transposed V row in LDS
-  constexpr int KCH = D / 8;       // 16-byte chunks per K row
-  constexpr int KLOADS = kKeys * KCH / kThreads;  // K vectors per thread per tile
-  constexpr int VK = kKeys * KCH / kThreads;      // V rows per thread per tile (same chunk)
-  constexpr int VGROUPS = kKeys / VK;             // V row groups per tile
-  static_assert(VK == 1 || VK == 2 || VK == 4, "V rows per thread");
+  // bf16 per V row in LDS: a 16-element shift of the banks per row keeps the
+  // transposing reads (four rows of 32 bytes per 16 lanes) conflict-free
+  constexpr int VPITCH = D + 16;
+  constexpr int KCH = D / 8;       // 8-element chunks per K / V row
+  constexpr int KLOADS = kKeys * KCH / kThreads;  // K (and V) chunks per thread per tile
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKeys * KPITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VPITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kKeys * VPITCH];
 
   // Workgroups are handed to the 8 XCDs round-robin by linear id, and each
   // XCD has its own L2. Route every kv head to one XCD (g % 8 == id % 8) and
@@ -205,38 +213,41 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   };
 
   // ---- tile fetch into registers ----
+  // Thread tid carries chunks tid + u * kThreads of the tile (row item / KCH,
+  // chunk item % KCH) for K and for V alike.
   KVec kreg[KLOADS];
-  KVec vreg[VK];
-  const int vkg = tid % VGROUPS;  // group of VK consecutive V rows of the item
-  const int vdc = tid / VGROUPS;  // 16-byte chunk of the V item
-  // Byte offsets of this thread's K and V vectors inside a contiguous tile
+  KVec vreg[KLOADS];
+  // Byte offsets of this thread's K and V chunks inside a contiguous tile
   // (rows x row stride + chunk: under 2^31 for any supported shape); fixed for
   // the whole kernel, so a tile fetch adds one uniform base.
   uint32_t koff[KLOADS];
-  uint32_t voff[VK];
+  uint32_t voff[KLOADS];
 #pragma unroll
   for (int u = 0; u < KLOADS; ++u) {
     const int item = tid + u * kThreads;
     koff[u] = static_cast<uint32_t>((item / KCH) * k_stride_bytes + (item % KCH) * CB);
+    voff[u] = static_cast<uint32_t>((item / KCH) * v_stride_bytes + (item % KCH) * CB);
   }
-#pragma unroll
-  for (int e = 0; e < VK; ++e)
-    voff[e] = static_cast<uint32_t>((vkg * VK + e) * v_stride_bytes + vdc * CB);
 
   auto fetch = [&](int kt0) {
     if (tile_contiguous) {
       // kt0 < Lk always, so the tile's first row exists
       const char* kb = paged ? k_cache + row_addr(kt0) : k_cache + (k0_row + kt0) * k_stride_bytes + head_off;
       const char* vb = paged ? v_cache + row_addr(kt0) : v_cache + (k0_row + kt0) * v_stride_bytes + head_off;
+      if (kt0 + kKeys <= Lk) {
+        // a full tile: no row can be past the keys
+#pragma unroll
+        for (int u = 0; u < KLOADS; ++u) {
+          kreg[u] = TV::load(kb + koff[u]);
+          vreg[u] = TV::load(vb + voff[u]);
+        }
+        return;
+      }
 #pragma unroll
       for (int u = 0; u < KLOADS; ++u) {
         const int key = kt0 + (tid + u * kThreads) / KCH;
         kreg[u] = key < Lk ? TV::load(kb + koff[u]) : KVec{};
-      }
-#pragma unroll
-      for (int e = 0; e < VK; ++e) {
-        const int key = kt0 + vkg * VK + e;
-        vreg[e] = key < Lk ? TV::load(vb + voff[e]) : KVec{};
+        vreg[u] = key < Lk ? TV::load(vb + voff[u]) : KVec{};
       }
       return;
     }
@@ -244,14 +255,12 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
     for (int u = 0; u < KLOADS; ++u) {
       const int item = tid + u * kThreads;
       const int key = kt0 + item / KCH;
-      kreg[u] = key < Lk ? TV::load(k_cache + row_addr(key) + (item % KCH) * CB) : KVec{};
-    }
-#pragma unroll
-    for (int e = 0; e < VK; ++e) {
-      const int key = kt0 + vkg * VK + e;
-      vreg[e] = key < Lk ? TV::load(v_cache + row_addr(key) + vdc * CB) : KVec{};
+      const int64_t ra = key < Lk ? row_addr(key) + (item % KCH) * CB : 0;
+      kreg[u] = key < Lk ? TV::load(k_cache + ra) : KVec{};
+      vreg[u] = key < Lk ? TV::load(v_cache + ra) : KVec{};
     }
   };
+  // K and V rows keep their natural [key][d] layout in LDS
   auto commit = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < KLOADS; ++u) {
@@ -259,25 +268,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
       const int r = item / KCH;
       const int c = item % KCH;
       *reinterpret_cast<Vec16*>(&sK[buf][r * KPITCH + c * 8]) = TV::to_bf16(kreg[u]);
-    }
-    Vec16 vb16[VK];
-#pragma unroll
-    for (int e = 0; e < VK; ++e) vb16[e] = TV::to_bf16(vreg[e]);
-    // V goes to LDS transposed: element j of the chunk is row vdc * 8 + j of
-    // sV, and the VK keys of this item sit side by side in that row
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint16_t* dst = &sV[buf][(vdc * 8 + j) * VPITCH + vkg * VK];
-      if constexpr (VK == 4) {
-        uint2 pk;
-        pk.x = half16(vb16[0], j) | (half16(vb16[1], j) << 16);
-        pk.y = half16(vb16[2], j) | (half16(vb16[3], j) << 16);
-        *reinterpret_cast<uint2*>(dst) = pk;
-      } else if constexpr (VK == 2) {
-        *reinterpret_cast<uint32_t*>(dst) = half16(vb16[0], j) | (half16(vb16[1], j) << 16);
-      } else {
-        *dst = static_cast<uint16_t>(half16(vb16[0], j));
-      }
+      *reinterpret_cast<Vec16*>(&sV[buf][r * VPITCH + c * 8]) = TV::to_bf16(vreg[u]);
     }
   };
 
@@ -371,15 +362,18 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
     }
 
     // O^T += V^T P^T
+    // A operand of lane (gq, col): V[key][dt * 16 + col] for the keys
+    // st * 32 + gq * 4 + 0..3 and st * 32 + 16 + gq * 4 + 0..3, the order in
+    // which the P^T operand holds them
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const uint16_t* vrow = &sV[buf][(dt * 16 + col) * VPITCH + st * 32 + gq * 4];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-        const Vec16 va{{lo.x, lo.y, hi.x, hi.y}};
-        const bf16x8_t a = as_bf16x8(va);
+        const uint16_t* vsrc = &sV[buf][(st * 32 + gq * 4 + (col >> 2)) * VPITCH + dt * 16 + 4 * (col & 3)];
+        const s16x4_t lo = ds_read_tr16(vsrc);
+        const s16x4_t hi = ds_read_tr16(vsrc + 16 * VPITCH);
+        const bf16x8_t a = __builtin_bit_cast(
+            bf16x8_t, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           o[dt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pop[st][t]), o[dt][t], 0, 0, 0);
