@@ -70,6 +70,26 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // (1.0, 1.0) in bf16
 
+// Fourth word of a raw buffer resource on gfx9-family parts (untyped 32-bit
+// data format); the offsets used are far below the record limit.
+constexpr int kBufferFlags = 0x00020000;
+
+// max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the lanes that hold
+// the same MFMA column), with the cross-row swaps v_permlane16_swap and
+// v_permlane32_swap: each returns the value and its partner's, in some order.
+__device__ __forceinline__ float col_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float col_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // a.x * b.x + a.y * b.y + c for packed bf16 pairs, fp32 accumulate
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -92,11 +112,23 @@ template <bool FP8> struct TileVec;
 template <> struct TileVec<false> {
   using Vec = Vec16;
   __device__ __forceinline__ static Vec load(const char* p) { return load16(p); }
+  // a tile row chunk at a 32-bit offset from a uniform base: buffer load with
+  // the base in scalar registers, so no 64-bit address arithmetic per lane
+  __device__ __forceinline__ static Vec load(__amdgpu_buffer_rsrc_t base, uint32_t off) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(base, off, 0, 0);
+    return Vec16{{v.x, v.y, v.z, v.w}};
+  }
   __device__ __forceinline__ static Vec16 to_bf16(const Vec& v) { return v; }
 };
 template <> struct TileVec<true> {
   using Vec = Vec8;
   __device__ __forceinline__ static Vec load(const char* p) { return load8(p); }
+  __device__ __forceinline__ static Vec load(__amdgpu_buffer_rsrc_t base, uint32_t off) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(base, off, 0, 0);
+    return Vec8{{v.x, v.y}};
+  }
   __device__ __forceinline__ static Vec16 to_bf16(const Vec& v) {
     return Vec16{{e4m3x2_to_bf16x2<false>(v.w[0]), e4m3x2_to_bf16x2<true>(v.w[0]),
                   e4m3x2_to_bf16x2<false>(v.w[1]), e4m3x2_to_bf16x2<true>(v.w[1])}};
@@ -236,10 +268,12 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
       const char* vb = paged ? v_cache + row_addr(kt0) : v_cache + (k0_row + kt0) * v_stride_bytes + head_off;
       if (kt0 + kKeys <= Lk) {
         // a full tile: no row can be past the keys
+        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kb), 0, 0x7fffffff, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vb), 0, 0x7fffffff, kBufferFlags);
 #pragma unroll
         for (int u = 0; u < KLOADS; ++u) {
-          kreg[u] = TV::load(kb + koff[u]);
-          vreg[u] = TV::load(vb + voff[u]);
+          kreg[u] = TV::load(kr, koff[u]);
+          vreg[u] = TV::load(vr, voff[u]);
         }
         return;
       }
@@ -328,8 +362,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
         tmax = fmaxf(tmax, fmaxf(fmaxf(s[kt][t][0], s[kt][t][1]), fmaxf(s[kt][t][2], s[kt][t][3])));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = col_max(tmax);
       const float m_new = fmaxf(m[t], tmax * scale_log2);
       // The O rows are rescaled only when some column's max moved; once the
       // first tiles have been seen that is rare.
@@ -387,9 +420,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   // ---- normalise and write ----
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    float lt = l[t];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    const float lt = col_sum(l[t]);
     if (orow[t] < 0) continue;
     const float inv = (FP8 ? v_scale : 1.f) / lt;
     uint16_t* orow_ptr = out + (static_cast<int64_t>(orow[t]) * num_q_heads + ohead[t]) * D;
