@@ -44,6 +44,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int kWavesPerGroup = 4;
@@ -74,14 +75,29 @@ constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // (1.0, 1.0) in bf16
 // data format); the offsets used are far below the record limit.
 constexpr int kBufferFlags = 0x00020000;
 
+// max of three floats in one v_max3_f32. Written as assembly because the
+// compiler, unable to prove MFMA results are canonical floats, otherwise
+// precedes every max with a canonicalising v_max(x, x); score tiles never hold
+// NaN (masked keys are -inf).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max2f(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the lanes that hold
 // the same MFMA column), with the cross-row swaps v_permlane16_swap and
 // v_permlane32_swap: each returns the value and its partner's, in some order.
 __device__ __forceinline__ float col_max(float v) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = max2f(__uint_as_float(a[0]), __uint_as_float(a[1]));
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max2f(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float col_sum(float v) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -104,6 +120,169 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 __device__ __forceinline__ s16x4_t ds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       reinterpret_cast<lds_s16x4_t*>(reinterpret_cast<uintptr_t>(p)));
+}
+
+// Online softmax over one 64-key tile of S^T for this wave's 32 (head,
+// query) columns, in the log2 domain: masks the keys a column may not see
+// (only on tiles that cross the causal diagonal or the end of the keys),
+// moves the running max m (the O rows and the sum l are rescaled only when
+// some column's max moved, which is rare once the first tiles are seen),
+// and leaves the weights as the bf16 P^T operand in pop[k-step][t], with l
+// summed from those same bf16 weights (what the PV product sees).
+template <int DT>
+__device__ __forceinline__ void softmax_max(f32x4_t (&s)[4][2], bool need_mask, const int (&posq)[2],
+                                            int Lk, int kt0, int gq, float scale_log2, float (&m)[2],
+                                            float (&l)[2], f32x4_t (&o)[DT][2]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (need_mask) {
+      // key kt0 + kt*16 + gq*4 + e is visible to this column iff it is at
+      // most lim (the query's position, capped by the last key)
+      const int lim = min(posq[t], Lk - 1) - (kt0 + gq * 4);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s[kt][t][e] = (kt * 16 + e <= lim) ? s[kt][t][e] : -INFINITY;
+    }
+    // raw-score max (scale > 0 keeps the order); masked keys are -inf
+    float tmax = max3f(s[0][t][0], s[0][t][1], s[0][t][2]);
+    tmax = max3f(tmax, s[0][t][3], s[1][t][0]);
+    tmax = max3f(tmax, s[1][t][1], s[1][t][2]);
+    tmax = max3f(tmax, s[1][t][3], s[2][t][0]);
+    tmax = max3f(tmax, s[2][t][1], s[2][t][2]);
+    tmax = max3f(tmax, s[2][t][3], s[3][t][0]);
+    tmax = max3f(tmax, s[3][t][1], s[3][t][2]);
+    tmax = max2f(tmax, s[3][t][3]);
+    tmax = col_max(tmax);
+    const float m_new = max2f(m[t], tmax * scale_log2);
+    if (__any(m_new != m[t])) {
+      const float alpha = fast_exp2(m[t] - m_new);
+      l[t] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt][t] *= alpha;
+    }
+    m[t] = m_new;
+  }
+}
+
+// Weights of a tile whose running max is already in m: exp2, bf16 P^T
+// operand, and the row sums (branch-free, so it can share a scheduling
+// region with independent matrix work).
+__device__ __forceinline__ void softmax_exp(f32x4_t (&s)[4][2], float scale_log2, const float (&m)[2],
+                                            float (&l)[2], Vec16 (&pop)[2][2]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[kt][t][e] = fast_exp2(fmaf(s[kt][t][e], scale_log2, -m[t]));
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      pop[st][t].w[0] = pack2(s[2 * st][t][0], s[2 * st][t][1]);
+      pop[st][t].w[1] = pack2(s[2 * st][t][2], s[2 * st][t][3]);
+      pop[st][t].w[2] = pack2(s[2 * st + 1][t][0], s[2 * st + 1][t][1]);
+      pop[st][t].w[3] = pack2(s[2 * st + 1][t][2], s[2 * st + 1][t][3]);
+    }
+    // two weights at a time with v_dot2 against (1, 1)
+    float lsum = l[t];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) lsum = dot2_bf16(pop[st][t].w[w], kOnesBf16x2, lsum);
+    l[t] = lsum;
+  }
+}
+
+// Online softmax over one 64-key tile of S^T for this wave's 32 (head,
+// query) columns, in the log2 domain: masks the keys a column may not see
+// (only on tiles that cross the causal diagonal or the end of the keys),
+// moves the running max m (the O rows and the sum l are rescaled only when
+// some column's max moved, which is rare once the first tiles are seen),
+// and leaves the weights as the bf16 P^T operand in pop[k-step][t], with l
+// summed from those same bf16 weights (what the PV product sees).
+template <int DT>
+__device__ __forceinline__ void softmax_tile(f32x4_t (&s)[4][2], bool need_mask, const int (&posq)[2],
+                                             int Lk, int kt0, int gq, float scale_log2, float (&m)[2],
+                                             float (&l)[2], f32x4_t (&o)[DT][2], Vec16 (&pop)[2][2]) {
+  softmax_max<DT>(s, need_mask, posq, Lk, kt0, gq, scale_log2, m, l, o);
+  softmax_exp(s, scale_log2, m, l, pop);
+}
+
+// Normalised bf16 output of this wave's two 16-column groups.
+template <int D>
+__device__ __forceinline__ void write_out(uint16_t* out, const f32x4_t (&o)[D / 16][2], const float (&l)[2],
+                                          const int (&orow)[2], const int (&ohead)[2], int num_q_heads,
+                                          int gq, float v_scale) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float lt = col_sum(l[t]);
+    if (orow[t] < 0) continue;
+    const float inv = v_scale / lt;
+    uint16_t* orow_ptr = out + (static_cast<int64_t>(orow[t]) * num_q_heads + ohead[t]) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      uint2 w;
+      w.x = pack2(o[dt][t][0] * inv, o[dt][t][1] * inv);
+      w.y = pack2(o[dt][t][2] * inv, o[dt][t][3] * inv);
+      *reinterpret_cast<uint2*>(orow_ptr + dt * 16 + gq * 4) = w;
+    }
+  }
+}
+
+// Workgroup -> (sequence i, kv head g, query tile x). Workgroups are handed
+// to the 8 XCDs round-robin by linear id, and each XCD has its own L2: every
+// kv head goes to one XCD (g % 8 == id % 8) and the query tiles of a
+// (sequence, kv head) sit next to each other, so the tiles that stream the
+// same K/V rows share an L2.
+__device__ __forceinline__ void tile_of_workgroup(int L, int num_kv_heads, int max_qt, int& i, int& g,
+                                                  int& x) {
+  if (num_kv_heads % kXcds == 0) {
+    const int xcd = L % kXcds;
+    const int r = L / kXcds;
+    const int heads_per_xcd = num_kv_heads / kXcds;
+    x = r % max_qt;
+    const int r2 = r / max_qt;
+    g = (r2 % heads_per_xcd) * kXcds + xcd;
+    i = r2 / heads_per_xcd;
+  } else {
+    x = L % max_qt;
+    const int r = L / max_qt;
+    g = r % num_kv_heads;
+    i = r / num_kv_heads;
+  }
+}
+
+// Q operands (B of S^T = K Q^T) of this wave's two 16-column groups: column
+// r of the workgroup's 128 is query head g * G + r / QT at query q_lo + r % QT
+// (heads of the group packed together), with its absolute position and its
+// output row (-1 for padding columns past the chunk).
+template <int D, int G>
+__device__ __forceinline__ void load_q(const char* q, int64_t q_stride_bytes, int q0, int Lq, int q_lo,
+                                       int start, int g, int wave, int col, int gq,
+                                       bf16x8_t (&qop)[2][D / 32], int (&posq)[2], int (&orow)[2],
+                                       int (&ohead)[2]) {
+  constexpr int QT = kRows / G;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int r = wave * 32 + t * 16 + col;
+    const int hl = r / QT;
+    const int ql = r % QT;
+    const int qi = q_lo + ql;
+    const int head = g * G + hl;
+    posq[t] = start + qi;
+    orow[t] = qi < Lq ? q0 + qi : -1;
+    ohead[t] = head;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      Vec16 v{{0u, 0u, 0u, 0u}};
+      if (qi < Lq) {
+        v = load16(q + static_cast<int64_t>(q0 + qi) * q_stride_bytes +
+                   (static_cast<int64_t>(head) * D + ks * 32 + gq * 8) * 2);
+      }
+      qop[t][ks] = as_bf16x8(v);
+    }
+  }
 }
 
 // Eight key / value elements as the tile loads carry them (bf16, or E4M3
@@ -159,28 +338,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKeys * KPITCH];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][kKeys * VPITCH];
 
-  // Workgroups are handed to the 8 XCDs round-robin by linear id, and each
-  // XCD has its own L2. Route every kv head to one XCD (g % 8 == id % 8) and
-  // put the query tiles of a (sequence, kv head) next to each other, so the
-  // tiles that stream the same K/V rows share an L2.
   int i, g, x;
-  {
-    const int L = blockIdx.x;
-    if (num_kv_heads % kXcds == 0) {
-      const int xcd = L % kXcds;
-      const int r = L / kXcds;
-      const int heads_per_xcd = num_kv_heads / kXcds;
-      x = r % max_qt;
-      const int r2 = r / max_qt;
-      g = (r2 % heads_per_xcd) * kXcds + xcd;
-      i = r2 / heads_per_xcd;
-    } else {
-      x = L % max_qt;
-      const int r = L / max_qt;
-      g = r % num_kv_heads;
-      i = r / num_kv_heads;
-    }
-  }
+  tile_of_workgroup(blockIdx.x, num_kv_heads, max_qt, i, g, x);
   const int q0 = cu_q[i];
   const int Lq = cu_q[i + 1] - q0;
   const int Lk = cu_k[i + 1] - cu_k[i];
@@ -204,26 +363,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   int posq[2];
   int orow[2];   // packed query row, -1 when this column is padding
   int ohead[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int r = wave * 32 + t * 16 + col;
-    const int hl = r / QT;
-    const int ql = r % QT;
-    const int qi = q_lo + ql;
-    const int head = g * G + hl;
-    posq[t] = start + qi;
-    orow[t] = qi < Lq ? q0 + qi : -1;
-    ohead[t] = head;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      Vec16 v{{0u, 0u, 0u, 0u}};
-      if (qi < Lq) {
-        v = load16(q + static_cast<int64_t>(q0 + qi) * q_stride_bytes +
-                   (static_cast<int64_t>(head) * D + ks * 32 + gq * 8) * 2);
-      }
-      qop[t][ks] = as_bf16x8(v);
-    }
-  }
+  load_q<D, G>(q, q_stride_bytes, q0, Lq, q_lo, start, g, wave, col, gq, qop, posq, orow, ohead);
 
   // Key rows come either from the paged caches (row stride H_kv * D) through
   // the block table, or, without a table, from packed k / v tensors where key
@@ -345,54 +485,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
 
     const bool need_mask = !(kt0 + kKeys - 1 <= start + q_lo && kt0 + kKeys <= Lk);
     Vec16 pop[2][2];  // [k-step of 32 keys][t]: P^T operand, 8 bf16
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (need_mask) {
-        // key kt0 + kt*16 + gq*4 + e is visible to this column iff it is at
-        // most lim (the query's position, capped by the last key)
-        const int lim = min(posq[t], Lk - 1) - (kt0 + gq * 4);
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            s[kt][t][e] = (kt * 16 + e <= lim) ? s[kt][t][e] : -INFINITY;
-      }
-      // raw-score max (scale > 0 keeps the order); masked keys are -inf
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        tmax = fmaxf(tmax, fmaxf(fmaxf(s[kt][t][0], s[kt][t][1]), fmaxf(s[kt][t][2], s[kt][t][3])));
-      tmax = col_max(tmax);
-      const float m_new = fmaxf(m[t], tmax * scale_log2);
-      // The O rows are rescaled only when some column's max moved; once the
-      // first tiles have been seen that is rare.
-      if (__any(m_new != m[t])) {
-        const float alpha = fast_exp2(m[t] - m_new);
-        l[t] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt][t] *= alpha;
-      }
-      m[t] = m_new;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[kt][t][e] = fast_exp2(fmaf(s[kt][t][e], scale_log2, -m_new));
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        pop[st][t].w[0] = pack2(s[2 * st][t][0], s[2 * st][t][1]);
-        pop[st][t].w[1] = pack2(s[2 * st][t][2], s[2 * st][t][3]);
-        pop[st][t].w[2] = pack2(s[2 * st + 1][t][0], s[2 * st + 1][t][1]);
-        pop[st][t].w[3] = pack2(s[2 * st + 1][t][2], s[2 * st + 1][t][3]);
-      }
-      // row sum of the weights as the PV product sees them (bf16), two at a
-      // time with v_dot2 against (1, 1)
-      float lsum = l[t];
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) lsum = dot2_bf16(pop[st][t].w[w], kOnesBf16x2, lsum);
-      l[t] = lsum;
-    }
+    softmax_tile<DT>(s, need_mask, posq, Lk, kt0, gq, scale_log2, m, l, o, pop);
 
     // O^T += V^T P^T
     // A operand of lane (gq, col): V[key][dt * 16 + col] for the keys
@@ -417,21 +510,249 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
     __syncthreads();
   }
 
-  // ---- normalise and write ----
+  write_out<D>(out, o, l, orow, ohead, num_q_heads, gq, FP8 ? v_scale : 1.f);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 caches, tiles of whole rows (packed K/V, or blocks of >= 64 keys):
+// K and V tiles travel from HBM straight into LDS (buffer loads with the LDS
+// destination), unpadded, with the 16-byte chunks of each row permuted by
+// kSwz so that the MFMA operand reads hit distinct banks. No tile passes
+// through registers, so the scores of the next tile fit beside the current
+// one: iteration j multiplies S(j+1) = K(j+1) Q^T while it turns S(j) into
+// weights, then adds P(j) V(j); the loads of K(j+2) and V(j+1) are issued at
+// its start and have the whole iteration to land.
+// ---------------------------------------------------------------------------
+
+// position of 16-byte chunk c of tile row r: c ^ kSwz(r) (conflict-free for
+// the 16-row K operand reads and the 4-row transposing V reads)
+template <int D>
+__device__ __forceinline__ int chunk_swz(int r) {
+  if constexpr (D == 128) {
+    return ((r & 7) << 1) | ((r >> 3) & 1);
+  } else {
+    return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+  }
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads, 2) prefill_direct_kernel(
+    uint16_t* __restrict__ out, const char* __restrict__ q, int64_t q_stride_bytes,
+    const char* __restrict__ k_cache, const char* __restrict__ v_cache, int64_t k_stride_bytes,
+    int64_t v_stride_bytes, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+    const int32_t* __restrict__ block_tables, int32_t max_blocks, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t log2_bs, float scale_log2, int32_t max_qt) {
+  constexpr int QT = kRows / G;      // queries per workgroup
+  constexpr int KS = D / 32;         // MFMA k-steps over head_dim
+  constexpr int DT = D / 16;         // 16-wide head_dim tiles of the output
+  constexpr int ROWB = D * 2;        // bytes per tile row
+  constexpr int NCH = ROWB / 16;     // 16-byte chunks per row
+  constexpr int LOADS = kKeys * ROWB / (kThreads * 16);  // 1 KiB wave loads per wave and tile
+  constexpr int ROWS_PER_LOAD = 1024 / ROWB;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKeys * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kKeys * D];
+
+  int i, g, x;
+  tile_of_workgroup(blockIdx.x, num_kv_heads, max_qt, i, g, x);
+  const int q0 = cu_q[i];
+  const int Lq = cu_q[i + 1] - q0;
+  const int Lk = cu_k[i + 1] - cu_k[i];
+  const int n_qt = (Lq + QT - 1) / QT;
+  if (x >= n_qt) return;
+  const int qt = n_qt - 1 - x;  // heaviest tiles first
+  const int q_lo = qt * QT;
+  const int q_hi = min(q_lo + QT, Lq);
+  const int start = Lk - Lq;
+  const int kmax = min(Lk, start + q_hi);
+  const int nkt = (kmax + kKeys - 1) / kKeys;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15;  // MFMA column / row-in-operand index
+  const int gq = lane >> 4;   // MFMA lane group
+
+  bf16x8_t qop[2][KS];
+  int posq[2];
+  int orow[2];
+  int ohead[2];
+  load_q<D, G>(q, q_stride_bytes, q0, Lq, q_lo, start, g, wave, col, gq, qop, posq, orow, ohead);
+
+  // Tile row r of key kt0 + r: paged rows of one block (block size >= 64, so
+  // a tile never straddles blocks), or packed rows cu_k[i] + kt0 + r.
+  const bool paged = block_tables != nullptr;
+  const int64_t head_off = static_cast<int64_t>(g) * ROWB;
+  const int32_t* table = paged ? block_tables + static_cast<int64_t>(i) * max_blocks : nullptr;
+  const int bs_mask = (1 << log2_bs) - 1;
+  const int64_t k0_row = paged ? 0 : cu_k[i];
+  auto tile_row0 = [&](int kt0) -> int64_t {  // row index of key kt0 in the K / V tensors
+    if (paged) {
+      // the block id is uniform: read it through the scalar cache (the
+      // compiler would make it a vector load behind the LDS-bound loads and
+      // wait for those)
+      const int32_t* e = table + (kt0 >> log2_bs);
+      int32_t blk;
+      asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(blk) : "s"(e) : "memory");
+      return (static_cast<int64_t>(blk) << log2_bs) + (kt0 & bs_mask);
+    }
+    return k0_row + kt0;
+  };
+
+  // This lane's part of wave load j: LDS bytes [(wave * LOADS + j) KiB +
+  // lane * 16, + 16) = tile row r, chunk position p, filled from chunk
+  // p ^ kSwz(r) of the row.
+  int lrow[LOADS];
+  uint32_t kload[LOADS], vload[LOADS];  // byte offsets inside a tile of whole rows
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const float lt = col_sum(l[t]);
-    if (orow[t] < 0) continue;
-    const float inv = (FP8 ? v_scale : 1.f) / lt;
-    uint16_t* orow_ptr = out + (static_cast<int64_t>(orow[t]) * num_q_heads + ohead[t]) * D;
+  for (int j = 0; j < LOADS; ++j) {
+    const int o = (wave * LOADS + j) * 1024 + lane * 16;
+    lrow[j] = o / ROWB;
+    const int p = (o % ROWB) / 16;
+    const uint32_t c = static_cast<uint32_t>(((p ^ chunk_swz<D>(lrow[j])) % NCH) * 16);
+    kload[j] = static_cast<uint32_t>(lrow[j] * k_stride_bytes) + c;
+    vload[j] = static_cast<uint32_t>(lrow[j] * v_stride_bytes) + c;
+  }
+  // The loads are written as inline assembly on purpose: the compiler would
+  // otherwise track the LDS they fill and wait for them before every LDS
+  // read of the other buffer. Their completion is awaited explicitly
+  // (s_waitcnt, then a barrier) before any wave reads what they filled.
+  // LDS byte address of this wave's first 1 KiB in each buffer (uniform)
+  auto wave_lds = [&](uint16_t* buf) -> uint32_t {
+    return __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(buf + wave * LOADS * 512)));
+  };
+  const uint32_t lds_k[2] = {wave_lds(sK[0]), wave_lds(sK[1])};
+  const uint32_t lds_v[2] = {wave_lds(sV[0]), wave_lds(sV[1])};
+  auto issue = [&](const char* base, int64_t stride, const uint32_t (&off)[LOADS], uint32_t lds, int kt0) {
+    const uint64_t tile = reinterpret_cast<uint64_t>(base + tile_row0(kt0) * stride + head_off);
+    u32x4_t rs;  // raw buffer resource: base, no stride, 2^31 - 1 bytes
+    rs.x = static_cast<uint32_t>(tile);
+    rs.y = static_cast<uint32_t>(tile >> 32) & 0xffffu;
+    rs.z = 0x7fffffffu;
+    rs.w = static_cast<uint32_t>(kBufferFlags);
+    if (kt0 + kKeys <= Lk) {
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j)
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :
+                     : "v"(off[j]), "s"(rs), "s"(lds + j * 1024)
+                     : "memory");
+      return;
+    }
+    // last tile: rows past the keys read the last key's row instead (its
+    // scores are masked and its weights are 0, and it is finite)
+    const int rmax = Lk - 1 - kt0;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const uint32_t o = lrow[j] <= rmax ? off[j] : off[j] - static_cast<uint32_t>((lrow[j] - rmax) * stride);
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                   :
+                   : "v"(o), "s"(rs), "s"(lds + j * 1024)
+                   : "memory");
+    }
+  };
+
+  // Loop-invariant LDS byte offsets of the operand reads. The swizzle of row
+  // r depends on r % 16 only, so rows that differ by whole 16-row steps
+  // (kt for K, st and the second half for V) reuse one offset plus an
+  // immediate.
+  //   K (A of S^T): lane (gq, col) reads row kt * 16 + col, chunk ks * 4 + gq
+  //   V (tr reads): lane m of group gq addresses row kbase + gq * 4 + m / 4,
+  //                 columns dt * 16 + 4 (m % 4) .. + 3
+  uint32_t krd[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    krd[ks] = static_cast<uint32_t>(col * ROWB + (((ks * 4 + gq) ^ chunk_swz<D>(col)) % NCH) * 16);
+  uint32_t vrd[DT];
+  {
+    const int rr = gq * 4 + (col >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      vrd[dt] = static_cast<uint32_t>(rr * ROWB + (((dt * 2 + ((col & 3) >> 1)) ^ chunk_swz<D>(rr)) % NCH) * 16 +
+                                      (col & 1) * 8);
+  }
+
+  // S^T tile from K rows in LDS
+  auto qk = [&](const uint16_t* kt_lds, f32x4_t (&s)[4][2]) {
+    const char* kb = reinterpret_cast<const char*>(kt_lds);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) s[kt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const bf16x8_t ka = as_bf16x8(*reinterpret_cast<const Vec16*>(kb + krd[ks] + kt * 16 * ROWB));
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          s[kt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qop[t][ks], s[kt][t], 0, 0, 0);
+      }
+    }
+  };
+
+  f32x4_t o[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) o[dt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY};
+  float l[2] = {0.f, 0.f};
+
+  issue(k_cache, k_stride_bytes, kload, lds_k[0], 0);
+  issue(v_cache, v_stride_bytes, vload, lds_v[0], 0);
+  if (nkt > 1) issue(k_cache, k_stride_bytes, kload, lds_k[1], kKeys);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x4_t s_cur[4][2];
+  qk(sK[0], s_cur);
+
+  for (int j = 0; j < nkt; ++j) {
+    const int kt0 = j * kKeys;
+    // everything issued in the previous iteration has landed, and every wave
+    // is done with K(j) (read for S(j) one iteration ago) and V(j - 1)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j + 2 < nkt) issue(k_cache, k_stride_bytes, kload, lds_k[j & 1], kt0 + 2 * kKeys);
+    if (j + 1 < nkt) issue(v_cache, v_stride_bytes, vload, lds_v[(j + 1) & 1], kt0 + kKeys);
+
+    const bool need_mask = !(kt0 + kKeys - 1 <= start + q_lo && kt0 + kKeys <= Lk);
+    softmax_max<DT>(s_cur, need_mask, posq, Lk, kt0, gq, scale_log2, m, l, o);
+
+    // the next tile's scores (matrix cores) beside this tile's exp2 /
+    // packing / row sums (vector ALU)
+    f32x4_t s_next[4][2];
+    if (j + 1 < nkt) qk(sK[(j + 1) & 1], s_next);
+    Vec16 pop[2][2];
+    softmax_exp(s_cur, scale_log2, m, l, pop);
+
+    // O^T += V^T P^T; lane (gq, col) takes column dt * 16 + col of the keys
+    // st * 32 + gq * 4 + 0..3 and st * 32 + 16 + gq * 4 + 0..3 (the order in
+    // which the P^T operand holds them)
+    const char* vt = reinterpret_cast<const char*>(sV[j & 1]);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      uint2 w;
-      w.x = pack2(o[dt][t][0] * inv, o[dt][t][1] * inv);
-      w.y = pack2(o[dt][t][2] * inv, o[dt][t][3] * inv);
-      *reinterpret_cast<uint2*>(orow_ptr + dt * 16 + gq * 4) = w;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const s16x4_t lo = ds_read_tr16(reinterpret_cast<const uint16_t*>(vt + vrd[dt] + st * 32 * ROWB));
+        const s16x4_t hi = ds_read_tr16(reinterpret_cast<const uint16_t*>(vt + vrd[dt] + (st * 32 + 16) * ROWB));
+        const bf16x8_t a = __builtin_bit_cast(
+            bf16x8_t, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          o[dt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pop[st][t]), o[dt][t], 0, 0, 0);
+      }
     }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) s_cur[kt][t] = s_next[kt][t];
   }
+
+  write_out<D>(out, o, l, orow, ohead, num_q_heads, gq, 1.f);
 }
 
 template <int D, int G, bool FP8>
@@ -447,6 +768,15 @@ hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
   dim3 grid(static_cast<uint32_t>(total));
   // an E4M3 cache holds K / k_scale: the score scale absorbs k_scale
   const float scale_log2 = a.scale * (FP8 ? a.k_scale : 1.f) * kLog2e;
+  const bool whole_rows = a.block_tables == nullptr || log2_bs >= 6;
+  if (!FP8 && whole_rows) {
+    hipLaunchKernelGGL((prefill_direct_kernel<D, G>), grid, dim3(kThreads), 0, stream,
+                       static_cast<uint16_t*>(a.out), static_cast<const char*>(a.q), a.q_stride * 2,
+                       static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache),
+                       a.k_stride * KB, a.v_stride * KB, a.cu_q, a.cu_k, a.block_tables, a.max_blocks,
+                       a.num_q_heads, a.num_kv_heads, log2_bs, scale_log2, max_qt);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((prefill_kernel<D, G, FP8>), grid, dim3(kThreads), 0, stream,
                      static_cast<uint16_t*>(a.out), static_cast<const char*>(a.q), a.q_stride * 2,
                      static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache),
