@@ -44,7 +44,6 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int kWavesPerGroup = 4;
@@ -167,8 +166,7 @@ __device__ __forceinline__ void softmax_max(f32x4_t (&s)[4][2], bool need_mask, 
 }
 
 // Weights of a tile whose running max is already in m: exp2, bf16 P^T
-// operand, and the row sums (branch-free, so it can share a scheduling
-// region with independent matrix work).
+// operand, and the row sums.
 __device__ __forceinline__ void softmax_exp(f32x4_t (&s)[4][2], float scale_log2, const float (&m)[2],
                                             float (&l)[2], Vec16 (&pop)[2][2]) {
 #pragma unroll
@@ -513,248 +511,6 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   write_out<D>(out, o, l, orow, ohead, num_q_heads, gq, FP8 ? v_scale : 1.f);
 }
 
-// ---------------------------------------------------------------------------
-// bf16 caches, tiles of whole rows (packed K/V, or blocks of >= 64 keys):
-// K and V tiles travel from HBM straight into LDS (buffer loads with the LDS
-// destination), unpadded, with the 16-byte chunks of each row permuted by
-// kSwz so that the MFMA operand reads hit distinct banks. No tile passes
-// through registers, so the scores of the next tile fit beside the current
-// one: iteration j multiplies S(j+1) = K(j+1) Q^T while it turns S(j) into
-// weights, then adds P(j) V(j); the loads of K(j+2) and V(j+1) are issued at
-// its start and have the whole iteration to land.
-// ---------------------------------------------------------------------------
-
-// position of 16-byte chunk c of tile row r: c ^ kSwz(r) (conflict-free for
-// the 16-row K operand reads and the 4-row transposing V reads)
-template <int D>
-__device__ __forceinline__ int chunk_swz(int r) {
-  if constexpr (D == 128) {
-    return ((r & 7) << 1) | ((r >> 3) & 1);
-  } else {
-    return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
-  }
-}
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-template <int D, int G>
-__global__ void __launch_bounds__(kThreads, 2) prefill_direct_kernel(
-    uint16_t* __restrict__ out, const char* __restrict__ q, int64_t q_stride_bytes,
-    const char* __restrict__ k_cache, const char* __restrict__ v_cache, int64_t k_stride_bytes,
-    int64_t v_stride_bytes, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
-    const int32_t* __restrict__ block_tables, int32_t max_blocks, int32_t num_q_heads,
-    int32_t num_kv_heads, int32_t log2_bs, float scale_log2, int32_t max_qt) {
-  constexpr int QT = kRows / G;      // queries per workgroup
-  constexpr int KS = D / 32;         // MFMA k-steps over head_dim
-  constexpr int DT = D / 16;         // 16-wide head_dim tiles of the output
-  constexpr int ROWB = D * 2;        // bytes per tile row
-  constexpr int NCH = ROWB / 16;     // 16-byte chunks per row
-  constexpr int LOADS = kKeys * ROWB / (kThreads * 16);  // 1 KiB wave loads per wave and tile
-  constexpr int ROWS_PER_LOAD = 1024 / ROWB;
-
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKeys * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kKeys * D];
-
-  int i, g, x;
-  tile_of_workgroup(blockIdx.x, num_kv_heads, max_qt, i, g, x);
-  const int q0 = cu_q[i];
-  const int Lq = cu_q[i + 1] - q0;
-  const int Lk = cu_k[i + 1] - cu_k[i];
-  const int n_qt = (Lq + QT - 1) / QT;
-  if (x >= n_qt) return;
-  const int qt = n_qt - 1 - x;  // heaviest tiles first
-  const int q_lo = qt * QT;
-  const int q_hi = min(q_lo + QT, Lq);
-  const int start = Lk - Lq;
-  const int kmax = min(Lk, start + q_hi);
-  const int nkt = (kmax + kKeys - 1) / kKeys;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int col = lane & 15;  // MFMA column / row-in-operand index
-  const int gq = lane >> 4;   // MFMA lane group
-
-  bf16x8_t qop[2][KS];
-  int posq[2];
-  int orow[2];
-  int ohead[2];
-  load_q<D, G>(q, q_stride_bytes, q0, Lq, q_lo, start, g, wave, col, gq, qop, posq, orow, ohead);
-
-  // Tile row r of key kt0 + r: paged rows of one block (block size >= 64, so
-  // a tile never straddles blocks), or packed rows cu_k[i] + kt0 + r.
-  const bool paged = block_tables != nullptr;
-  const int64_t head_off = static_cast<int64_t>(g) * ROWB;
-  const int32_t* table = paged ? block_tables + static_cast<int64_t>(i) * max_blocks : nullptr;
-  const int bs_mask = (1 << log2_bs) - 1;
-  const int64_t k0_row = paged ? 0 : cu_k[i];
-  auto tile_row0 = [&](int kt0) -> int64_t {  // row index of key kt0 in the K / V tensors
-    if (paged) {
-      // the block id is uniform: read it through the scalar cache (the
-      // compiler would make it a vector load behind the LDS-bound loads and
-      // wait for those)
-      const int32_t* e = table + (kt0 >> log2_bs);
-      int32_t blk;
-      asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(blk) : "s"(e) : "memory");
-      return (static_cast<int64_t>(blk) << log2_bs) + (kt0 & bs_mask);
-    }
-    return k0_row + kt0;
-  };
-
-  // This lane's part of wave load j: LDS bytes [(wave * LOADS + j) KiB +
-  // lane * 16, + 16) = tile row r, chunk position p, filled from chunk
-  // p ^ kSwz(r) of the row.
-  int lrow[LOADS];
-  uint32_t kload[LOADS], vload[LOADS];  // byte offsets inside a tile of whole rows
-#pragma unroll
-  for (int j = 0; j < LOADS; ++j) {
-    const int o = (wave * LOADS + j) * 1024 + lane * 16;
-    lrow[j] = o / ROWB;
-    const int p = (o % ROWB) / 16;
-    const uint32_t c = static_cast<uint32_t>(((p ^ chunk_swz<D>(lrow[j])) % NCH) * 16);
-    kload[j] = static_cast<uint32_t>(lrow[j] * k_stride_bytes) + c;
-    vload[j] = static_cast<uint32_t>(lrow[j] * v_stride_bytes) + c;
-  }
-  // The loads are written as inline assembly on purpose: the compiler would
-  // otherwise track the LDS they fill and wait for them before every LDS
-  // read of the other buffer. Their completion is awaited explicitly
-  // (s_waitcnt, then a barrier) before any wave reads what they filled.
-  // LDS byte address of this wave's first 1 KiB in each buffer (uniform)
-  auto wave_lds = [&](uint16_t* buf) -> uint32_t {
-    return __builtin_amdgcn_readfirstlane(
-        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(buf + wave * LOADS * 512)));
-  };
-  const uint32_t lds_k[2] = {wave_lds(sK[0]), wave_lds(sK[1])};
-  const uint32_t lds_v[2] = {wave_lds(sV[0]), wave_lds(sV[1])};
-  auto issue = [&](const char* base, int64_t stride, const uint32_t (&off)[LOADS], uint32_t lds, int kt0) {
-    const uint64_t tile = reinterpret_cast<uint64_t>(base + tile_row0(kt0) * stride + head_off);
-    u32x4_t rs;  // raw buffer resource: base, no stride, 2^31 - 1 bytes
-    rs.x = static_cast<uint32_t>(tile);
-    rs.y = static_cast<uint32_t>(tile >> 32) & 0xffffu;
-    rs.z = 0x7fffffffu;
-    rs.w = static_cast<uint32_t>(kBufferFlags);
-    if (kt0 + kKeys <= Lk) {
-#pragma unroll
-      for (int j = 0; j < LOADS; ++j)
-        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                     :
-                     : "v"(off[j]), "s"(rs), "s"(lds + j * 1024)
-                     : "memory");
-      return;
-    }
-    // last tile: rows past the keys read the last key's row instead (its
-    // scores are masked and its weights are 0, and it is finite)
-    const int rmax = Lk - 1 - kt0;
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-      const uint32_t o = lrow[j] <= rmax ? off[j] : off[j] - static_cast<uint32_t>((lrow[j] - rmax) * stride);
-      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                   :
-                   : "v"(o), "s"(rs), "s"(lds + j * 1024)
-                   : "memory");
-    }
-  };
-
-  // Loop-invariant LDS byte offsets of the operand reads. The swizzle of row
-  // r depends on r % 16 only, so rows that differ by whole 16-row steps
-  // (kt for K, st and the second half for V) reuse one offset plus an
-  // immediate.
-  //   K (A of S^T): lane (gq, col) reads row kt * 16 + col, chunk ks * 4 + gq
-  //   V (tr reads): lane m of group gq addresses row kbase + gq * 4 + m / 4,
-  //                 columns dt * 16 + 4 (m % 4) .. + 3
-  uint32_t krd[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    krd[ks] = static_cast<uint32_t>(col * ROWB + (((ks * 4 + gq) ^ chunk_swz<D>(col)) % NCH) * 16);
-  uint32_t vrd[DT];
-  {
-    const int rr = gq * 4 + (col >> 2);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      vrd[dt] = static_cast<uint32_t>(rr * ROWB + (((dt * 2 + ((col & 3) >> 1)) ^ chunk_swz<D>(rr)) % NCH) * 16 +
-                                      (col & 1) * 8);
-  }
-
-  // S^T tile from K rows in LDS
-  auto qk = [&](const uint16_t* kt_lds, f32x4_t (&s)[4][2]) {
-    const char* kb = reinterpret_cast<const char*>(kt_lds);
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) s[kt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const bf16x8_t ka = as_bf16x8(*reinterpret_cast<const Vec16*>(kb + krd[ks] + kt * 16 * ROWB));
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          s[kt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qop[t][ks], s[kt][t], 0, 0, 0);
-      }
-    }
-  };
-
-  f32x4_t o[DT][2];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) o[dt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {-INFINITY, -INFINITY};
-  float l[2] = {0.f, 0.f};
-
-  issue(k_cache, k_stride_bytes, kload, lds_k[0], 0);
-  issue(v_cache, v_stride_bytes, vload, lds_v[0], 0);
-  if (nkt > 1) issue(k_cache, k_stride_bytes, kload, lds_k[1], kKeys);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  f32x4_t s_cur[4][2];
-  qk(sK[0], s_cur);
-
-  for (int j = 0; j < nkt; ++j) {
-    const int kt0 = j * kKeys;
-    // everything issued in the previous iteration has landed, and every wave
-    // is done with K(j) (read for S(j) one iteration ago) and V(j - 1)
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (j + 2 < nkt) issue(k_cache, k_stride_bytes, kload, lds_k[j & 1], kt0 + 2 * kKeys);
-    if (j + 1 < nkt) issue(v_cache, v_stride_bytes, vload, lds_v[(j + 1) & 1], kt0 + kKeys);
-
-    const bool need_mask = !(kt0 + kKeys - 1 <= start + q_lo && kt0 + kKeys <= Lk);
-    softmax_max<DT>(s_cur, need_mask, posq, Lk, kt0, gq, scale_log2, m, l, o);
-
-    // the next tile's scores (matrix cores) beside this tile's exp2 /
-    // packing / row sums (vector ALU)
-    f32x4_t s_next[4][2];
-    if (j + 1 < nkt) qk(sK[(j + 1) & 1], s_next);
-    Vec16 pop[2][2];
-    softmax_exp(s_cur, scale_log2, m, l, pop);
-
-    // O^T += V^T P^T; lane (gq, col) takes column dt * 16 + col of the keys
-    // st * 32 + gq * 4 + 0..3 and st * 32 + 16 + gq * 4 + 0..3 (the order in
-    // which the P^T operand holds them)
-    const char* vt = reinterpret_cast<const char*>(sV[j & 1]);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const s16x4_t lo = ds_read_tr16(reinterpret_cast<const uint16_t*>(vt + vrd[dt] + st * 32 * ROWB));
-        const s16x4_t hi = ds_read_tr16(reinterpret_cast<const uint16_t*>(vt + vrd[dt] + (st * 32 + 16) * ROWB));
-        const bf16x8_t a = __builtin_bit_cast(
-            bf16x8_t, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          o[dt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pop[st][t]), o[dt][t], 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) s_cur[kt][t] = s_next[kt][t];
-  }
-
-  write_out<D>(out, o, l, orow, ohead, num_q_heads, gq, 1.f);
-}
-
 template <int D, int G, bool FP8>
 hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
   constexpr int KB = FP8 ? 1 : 2;
@@ -768,15 +524,6 @@ hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
   dim3 grid(static_cast<uint32_t>(total));
   // an E4M3 cache holds K / k_scale: the score scale absorbs k_scale
   const float scale_log2 = a.scale * (FP8 ? a.k_scale : 1.f) * kLog2e;
-  const bool whole_rows = a.block_tables == nullptr || log2_bs >= 6;
-  if (!FP8 && whole_rows) {
-    hipLaunchKernelGGL((prefill_direct_kernel<D, G>), grid, dim3(kThreads), 0, stream,
-                       static_cast<uint16_t*>(a.out), static_cast<const char*>(a.q), a.q_stride * 2,
-                       static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache),
-                       a.k_stride * KB, a.v_stride * KB, a.cu_q, a.cu_k, a.block_tables, a.max_blocks,
-                       a.num_q_heads, a.num_kv_heads, log2_bs, scale_log2, max_qt);
-    return hipGetLastError();
-  }
   hipLaunchKernelGGL((prefill_kernel<D, G, FP8>), grid, dim3(kThreads), 0, stream,
                      static_cast<uint16_t*>(a.out), static_cast<const char*>(a.q), a.q_stride * 2,
                      static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache),
