@@ -70,6 +70,10 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // (1.0, 1.0) in bf16
 
+// Headroom of the running softmax max, in log2 units: tile weights may reach
+// 2^kMaxSlack before the max is moved.
+constexpr float kMaxSlack = 8.f;
+
 // Fourth word of a raw buffer resource on gfx9-family parts (untyped 32-bit
 // data format); the offsets used are far below the record limit.
 constexpr int kBufferFlags = 0x00020000;
@@ -124,8 +128,8 @@ __device__ __forceinline__ s16x4_t ds_read_tr16(const uint16_t* p) {
 // Online softmax over one 64-key tile of S^T for this wave's 32 (head,
 // query) columns, in the log2 domain: masks the keys a column may not see
 // (only on tiles that cross the causal diagonal or the end of the keys),
-// moves the running max m (the O rows and the sum l are rescaled only when
-// some column's max moved, which is rare once the first tiles are seen),
+// moves the running max m when a column's max outgrows it by more than
+// kMaxSlack (the O rows and the sum l are rescaled on those tiles only),
 // and leaves the weights as the bf16 P^T operand in pop[k-step][t], with l
 // summed from those same bf16 weights (what the PV product sees).
 template <int DT>
@@ -154,14 +158,20 @@ __device__ __forceinline__ void softmax_max(f32x4_t (&s)[4][2], bool need_mask, 
     tmax = max3f(tmax, s[3][t][1], s[3][t][2]);
     tmax = max2f(tmax, s[3][t][3]);
     tmax = col_max(tmax);
-    const float m_new = max2f(m[t], tmax * scale_log2);
-    if (__any(m_new != m[t])) {
+    // The reference max moves only when some column's max exceeds it by more
+    // than kMaxSlack (log2 units); otherwise the tile's weights are taken
+    // against the old max and stay below 2^kMaxSlack. Softmax does not
+    // depend on that reference, and fp32 sums and bf16 weights have the range
+    // for it, so O and l are rescaled on the few tiles that move it.
+    const float m_cand = tmax * scale_log2;
+    if (__any(m_cand > m[t] + kMaxSlack)) {
+      const float m_new = max2f(m[t], m_cand);
       const float alpha = fast_exp2(m[t] - m_new);
       l[t] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt][t] *= alpha;
+      m[t] = m_new;
     }
-    m[t] = m_new;
   }
 }
 
@@ -195,8 +205,8 @@ __device__ __forceinline__ void softmax_exp(f32x4_t (&s)[4][2], float scale_log2
 // Online softmax over one 64-key tile of S^T for this wave's 32 (head,
 // query) columns, in the log2 domain: masks the keys a column may not see
 // (only on tiles that cross the causal diagonal or the end of the keys),
-// moves the running max m (the O rows and the sum l are rescaled only when
-// some column's max moved, which is rare once the first tiles are seen),
+// moves the running max m when a column's max outgrows it by more than
+// kMaxSlack (the O rows and the sum l are rescaled on those tiles only),
 // and leaves the weights as the bf16 P^T operand in pop[k-step][t], with l
 // summed from those same bf16 weights (what the PV product sees).
 template <int DT>

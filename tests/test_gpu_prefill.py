@@ -23,9 +23,9 @@ def _views(qkv, w):
             qkv[:, (hq + hkv) * d:].view(t, hkv, d))
 
 
-def run_small(w):
+def run_small(w, t=None):
     import torch
-    t = wl.make_host_tensors(w)
+    t = wl.make_host_tensors(w) if t is None else t
     qkv = to_device(t["qkv"], w.dtype)
     q, k, v = _views(qkv, w)
     kc = to_device(t["k_cache"], w.dtype)
@@ -70,6 +70,35 @@ def test_prefill_block_sizes(bs, cached, sched):
     w = wl.custom_prefill(cached, sched, block_size=bs, num_q_heads=32, num_kv_heads=8,
                           head_dim=128, dtype="bf16", seed=bs)
     run_small(w)
+
+
+def _scale_key_rows(t, w, seq, factor):
+    """Multiply the K row at every key position p of sequence ``seq`` by
+    factor(p), in the cache (cached positions) and in the new rows."""
+    bs = w.block_size
+    cached = int(w.num_cached[seq])
+    q0 = int(w.cu_seqlens_q[seq])
+    for p in range(cached + int(w.num_scheduled[seq])):
+        f = np.float32(factor(p))
+        if p < cached:
+            blk, r = int(w.block_tables[seq][p // bs]), p % bs
+            row = t["k_cache"][blk, r]
+        else:
+            row = t["k"][q0 + p - cached]
+        row[...] = wl.f32_to_bf16_bits(widen_host(row, "bf16").astype(np.float32) * f)
+
+
+def test_prefill_running_max_moves():
+    """Key rows whose scores grow tile by tile (and jump, then fall back, on
+    one tile): the running max moves by small steps that stay within the
+    kernel's headroom, by steps beyond it, and later tiles carry weights far
+    below the max."""
+    w = wl.custom_prefill([600, 64], [300, 200], block_size=64, num_q_heads=8, num_kv_heads=2,
+                          head_dim=128, dtype="bf16", seed=11)
+    t = wl.make_host_tensors(w)
+    for seq in range(2):
+        _scale_key_rows(t, w, seq, lambda p: (1.0 + 0.35 * (p // 64)) * (2.5 if p // 64 == 9 else 1.0))
+    run_small(w, t)
 
 
 def test_prefill_shared_prefix():
