@@ -240,10 +240,12 @@ def run_prefill(torch, binding, wl, w, steps, warmup, flush, scratch):
     return res
 
 
-def run_graph_small(torch, binding, wl, steps=200):
-    """Small decode batches are launch-bound: time back-to-back steps
-    (pa_store_kvcache + pa_decode) issued eagerly and as one HIP-graph replay
-    per step, wall clock over the whole run, no cache eviction."""
+def run_graph_small(torch, binding, wl, steps=100):
+    """Small decode batches are launch-bound: time back-to-back steps issued
+    eagerly and as one HIP-graph replay per step, wall clock over the whole
+    run, no cache eviction. A step is the attention of 1 layer, or of the 28
+    layers of a Qwen3-0.6B-shaped model (each layer its own cache), as a
+    serving engine captures the whole decode forward per batch bucket."""
     w = wl.custom_decode([512] * 8, block_size=256, num_q_heads=16, num_kv_heads=8, head_dim=128,
                          dtype="bf16", seed=5, width=2)
     t = wl.make_device_tensors(w)
@@ -254,42 +256,51 @@ def run_graph_small(torch, binding, wl, steps=200):
     need = binding.pa_decode_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                             w.block_size, w.max_blocks_per_seq, 0)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    n_layers = 28
+    caches = [(t["k_cache"].clone(), t["v_cache"].clone()) for _ in range(n_layers)]
 
-    def step():
-        binding.pa_store_kvcache(t["k"], t["v"], t["k_cache"], t["v_cache"], slots)
-        binding.pa_decode(t["q"], t["k_cache"], t["v_cache"], tables, ctx, w.scale, out=out,
-                          workspace=ws)
+    def step(layers):
+        def run():
+            for kc, vc in caches[:layers]:
+                binding.pa_store_kvcache(t["k"], t["v"], kc, vc, slots)
+                binding.pa_decode(t["q"], kc, vc, tables, ctx, w.scale, out=out, workspace=ws)
+        return run
 
-    def fused():
-        binding.pa_store_decode(t["q"], t["k"], t["v"], slots, t["k_cache"], t["v_cache"], tables, ctx,
-                                w.scale, out=out, workspace=ws)
+    def fused(layers):
+        def run():
+            for kc, vc in caches[:layers]:
+                binding.pa_store_decode(t["q"], t["k"], t["v"], slots, kc, vc, tables, ctx, w.scale,
+                                        out=out, workspace=ws)
+        return run
 
-    graphs = {}
-    for name, fn in (("graph", step), ("graph_fused", fused)):
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for _ in range(3):
-                fn()
-        torch.cuda.current_stream().wait_stream(side)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            fn()
-        graphs[name] = g
-    torch.cuda.synchronize()
     res = {}
-    for name, fn in (("eager", step), ("eager_fused", fused), ("graph", graphs["graph"].replay),
-                     ("graph_fused", graphs["graph_fused"].replay)):
-        for _ in range(10):
-            fn()
+    for layers in (1, n_layers):
+        fns = {"eager": step(layers), "eager_fused": fused(layers)}
+        for name in ("eager", "eager_fused"):
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for _ in range(3):
+                    fns[name]()
+            torch.cuda.current_stream().wait_stream(side)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fns[name]()
+            fns[name.replace("eager", "graph")] = g.replay
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            fn()
-        torch.cuda.synchronize()
-        res[f"{name}_us_per_step"] = round((time.perf_counter() - t0) / steps * 1e6, 2)
-    res["workload"] = "8 seqs x 512 tokens, qwen3-0.6b shapes, store + decode per step"
-    del t
+        for name in ("eager", "eager_fused", "graph", "graph_fused"):
+            fn = fns[name]
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                fn()
+            torch.cuda.synchronize()
+            res[f"{layers}L_{name}_us_per_step"] = round((time.perf_counter() - t0) / steps * 1e6, 2)
+    res["workload"] = ("8 seqs x 512 tokens, qwen3-0.6b attention shapes; per step 1 layer or 28 layers "
+                       "of store + decode (two calls, or the fused call)")
+    del t, caches
     return res
 
 

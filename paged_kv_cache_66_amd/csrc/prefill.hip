@@ -463,8 +463,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   float l[2] = {0.f, 0.f};
 
   // Tile j is multiplied from LDS buffer j % 2 while tile j + 1 travels from
-  // HBM into registers; it is written to the other buffer afterwards, and a
-  // single barrier per tile separates the writes from the next reads.
+  // HBM into registers; it is written to the other buffer after the softmax,
+  // and a single barrier per tile separates the writes from the next reads.
   fetch(0);
   commit(0);
   __syncthreads();
@@ -494,6 +494,10 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
     const bool need_mask = !(kt0 + kKeys - 1 <= start + q_lo && kt0 + kKeys <= Lk);
     Vec16 pop[2][2];  // [k-step of 32 keys][t]: P^T operand, 8 bf16
     softmax_tile<DT>(s, need_mask, posq, Lk, kt0, gq, scale_log2, m, l, o, pop);
+    // the next tile goes to the other buffer (free since the last barrier)
+    // here, between the softmax and P V, rather than in a burst before the
+    // barrier
+    if (j + 1 < nkt) commit(buf ^ 1);
 
     // O^T += V^T P^T
     // A operand of lane (gq, col): V[key][dt * 16 + col] for the keys
@@ -514,7 +518,6 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
         }
       }
     }
-    if (j + 1 < nkt) commit(buf ^ 1);
     __syncthreads();
   }
 
