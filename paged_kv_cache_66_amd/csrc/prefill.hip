@@ -26,11 +26,16 @@
 // * online softmax in the log2 domain: the running max is taken on raw
 //   scores and the scale is folded into the one FMA that feeds exp2; only the
 //   tiles that cross the causal diagonal or the end of the keys are masked;
-// * K/V tiles are double-buffered in LDS: the next tile's rows travel from
-//   HBM into registers while the current tile is multiplied, and one barrier
-//   per tile separates the buffer writes from the reads. Tiles that lie
-//   wholly inside the keys (all but the last) are fetched without per-row
-//   bounds checks.
+// * K/V tiles are double-buffered in LDS, with one barrier per tile. Two
+//   kernels: bf16 tiles of whole rows (packed K/V, or blocks of at least one
+//   tile) go from HBM straight into LDS (buffer loads with the LDS
+//   destination), which leaves the registers to hold the next tile's scores
+//   beside the current softmax, and each wave interleaves its MFMAs with the
+//   softmax by hand (prefill_direct_kernel, below); E4M3 caches and blocks
+//   shorter than a tile stage the rows in registers (prefill_kernel): the
+//   next tile's rows travel from HBM into registers while the current tile
+//   is multiplied. Tiles that lie wholly inside the keys (all but the last)
+//   are fetched without per-row bounds checks.
 // * E4M3 caches (FP8): tiles travel as one-byte codes and are widened to bf16
 //   (exactly) on their way into LDS; k_scale joins the softmax scale and
 //   v_scale the final normalisation.
@@ -45,6 +50,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWavesPerGroup = 4;
 constexpr int kThreads = 64 * kWavesPerGroup;
@@ -524,6 +530,383 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   write_out<D>(out, o, l, orow, ohead, num_q_heads, gq, FP8 ? v_scale : 1.f);
 }
 
+// ---------------------------------------------------------------------------
+// bf16 caches, tiles of whole rows (packed K/V, or blocks of >= 64 keys):
+// K and V tiles travel from HBM straight into LDS (buffer loads with the LDS
+// destination), unpadded, with the 16-byte chunks of each row permuted by
+// chunk_swz so that the MFMA operand reads hit distinct banks. No tile passes
+// through registers, so the scores of the next tile fit beside the current
+// one, and each wave interleaves its matrix and vector work by hand:
+// iteration j forms S(j+1) = K(j+1) Q^T with three softmax instructions of
+// tile j (exp2, packing, row sums) after every MFMA, then adds P(j) V(j) with
+// the pieces of tile j+1's max between the MFMAs; the loads of K(j+2) and
+// V(j+1) are issued at its start and have the whole iteration to land.
+// ---------------------------------------------------------------------------
+
+// position of 16-byte chunk c of tile row r: c ^ kSwz(r) (conflict-free for
+// the 16-row K operand reads and the 4-row transposing V reads)
+template <int D>
+__device__ __forceinline__ int chunk_swz(int r) {
+  if constexpr (D == 128) {
+    return ((r & 7) << 1) | ((r >> 3) & 1);
+  } else {
+    return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+  }
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads, 2) prefill_direct_kernel(
+    uint16_t* __restrict__ out, const char* __restrict__ q, int64_t q_stride_bytes,
+    const char* __restrict__ k_cache, const char* __restrict__ v_cache, int64_t k_stride_bytes,
+    int64_t v_stride_bytes, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+    const int32_t* __restrict__ block_tables, int32_t max_blocks, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t log2_bs, float scale_log2, int32_t max_qt) {
+  constexpr int QT = kRows / G;      // queries per workgroup
+  constexpr int KS = D / 32;         // MFMA k-steps over head_dim
+  constexpr int DT = D / 16;         // 16-wide head_dim tiles of the output
+  constexpr int ROWB = D * 2;        // bytes per tile row
+  constexpr int NCH = ROWB / 16;     // 16-byte chunks per row
+  constexpr int LOADS = kKeys * ROWB / (kThreads * 16);  // 1 KiB wave loads per wave and tile
+  constexpr int ROWS_PER_LOAD = 1024 / ROWB;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKeys * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kKeys * D];
+
+  int i, g, x;
+  tile_of_workgroup(blockIdx.x, num_kv_heads, max_qt, i, g, x);
+  const int q0 = cu_q[i];
+  const int Lq = cu_q[i + 1] - q0;
+  const int Lk = cu_k[i + 1] - cu_k[i];
+  const int n_qt = (Lq + QT - 1) / QT;
+  if (x >= n_qt) return;
+  const int qt = n_qt - 1 - x;  // heaviest tiles first
+  const int q_lo = qt * QT;
+  const int q_hi = min(q_lo + QT, Lq);
+  const int start = Lk - Lq;
+  const int kmax = min(Lk, start + q_hi);
+  const int nkt = (kmax + kKeys - 1) / kKeys;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15;  // MFMA column / row-in-operand index
+  const int gq = lane >> 4;   // MFMA lane group
+
+  bf16x8_t qop[2][KS];
+  int posq[2];
+  int orow[2];
+  int ohead[2];
+  load_q<D, G>(q, q_stride_bytes, q0, Lq, q_lo, start, g, wave, col, gq, qop, posq, orow, ohead);
+
+  // Tile row r of key kt0 + r: paged rows of one block (block size >= 64, so
+  // a tile never straddles blocks), or packed rows cu_k[i] + kt0 + r.
+  const bool paged = block_tables != nullptr;
+  const int64_t head_off = static_cast<int64_t>(g) * ROWB;
+  const int32_t* table = paged ? block_tables + static_cast<int64_t>(i) * max_blocks : nullptr;
+  const int bs_mask = (1 << log2_bs) - 1;
+  const int64_t k0_row = paged ? 0 : cu_k[i];
+  auto tile_row0 = [&](int kt0) -> int64_t {  // row index of key kt0 in the K / V tensors
+    if (paged) {
+      // the block id is uniform: read it through the scalar cache (the
+      // compiler would make it a vector load behind the LDS-bound loads and
+      // wait for those)
+      const int32_t* e = table + (kt0 >> log2_bs);
+      int32_t blk;
+      asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(blk) : "s"(e) : "memory");
+      return (static_cast<int64_t>(blk) << log2_bs) + (kt0 & bs_mask);
+    }
+    return k0_row + kt0;
+  };
+
+  // This lane's part of wave load j: LDS bytes [(wave * LOADS + j) KiB +
+  // lane * 16, + 16) = tile row r, chunk position p, filled from chunk
+  // p ^ kSwz(r) of the row.
+  int lrow[LOADS];
+  uint32_t kload[LOADS], vload[LOADS];  // byte offsets inside a tile of whole rows
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int o = (wave * LOADS + j) * 1024 + lane * 16;
+    lrow[j] = o / ROWB;
+    const int p = (o % ROWB) / 16;
+    const uint32_t c = static_cast<uint32_t>(((p ^ chunk_swz<D>(lrow[j])) % NCH) * 16);
+    kload[j] = static_cast<uint32_t>(lrow[j] * k_stride_bytes) + c;
+    vload[j] = static_cast<uint32_t>(lrow[j] * v_stride_bytes) + c;
+  }
+  // The loads are written as inline assembly on purpose: the compiler would
+  // otherwise track the LDS they fill and wait for them before every LDS
+  // read of the other buffer. Their completion is awaited explicitly
+  // (s_waitcnt, then a barrier) before any wave reads what they filled.
+  // LDS byte address of this wave's first 1 KiB in each buffer (uniform)
+  auto wave_lds = [&](uint16_t* buf) -> uint32_t {
+    return __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(buf + wave * LOADS * 512)));
+  };
+  const uint32_t lds_k[2] = {wave_lds(sK[0]), wave_lds(sK[1])};
+  const uint32_t lds_v[2] = {wave_lds(sV[0]), wave_lds(sV[1])};
+  auto issue = [&](const char* base, int64_t stride, const uint32_t (&off)[LOADS], uint32_t lds, int kt0) {
+    const uint64_t tile = reinterpret_cast<uint64_t>(base + tile_row0(kt0) * stride + head_off);
+    u32x4_t rs;  // raw buffer resource: base, no stride, 2^31 - 1 bytes
+    rs.x = static_cast<uint32_t>(tile);
+    rs.y = static_cast<uint32_t>(tile >> 32) & 0xffffu;
+    rs.z = 0x7fffffffu;
+    rs.w = static_cast<uint32_t>(kBufferFlags);
+    if (kt0 + kKeys <= Lk) {
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j)
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :
+                     : "v"(off[j]), "s"(rs), "s"(lds + j * 1024)
+                     : "memory");
+      return;
+    }
+    // last tile: rows past the keys read the last key's row instead (its
+    // scores are masked and its weights are 0, and it is finite)
+    const int rmax = Lk - 1 - kt0;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const uint32_t o = lrow[j] <= rmax ? off[j] : off[j] - static_cast<uint32_t>((lrow[j] - rmax) * stride);
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                   :
+                   : "v"(o), "s"(rs), "s"(lds + j * 1024)
+                   : "memory");
+    }
+  };
+
+  // Loop-invariant LDS byte offsets of the operand reads. The swizzle of row
+  // r depends on r % 16 only, so rows that differ by whole 16-row steps
+  // (kt for K, st and the second half for V) reuse one offset plus an
+  // immediate.
+  //   K (A of S^T): lane (gq, col) reads row kt * 16 + col, chunk ks * 4 + gq
+  //   V (tr reads): lane m of group gq addresses row kbase + gq * 4 + m / 4,
+  //                 columns dt * 16 + 4 (m % 4) .. + 3
+  uint32_t krd[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    krd[ks] = static_cast<uint32_t>(col * ROWB + (((ks * 4 + gq) ^ chunk_swz<D>(col)) % NCH) * 16);
+  uint32_t vrd[DT];
+  {
+    const int rr = gq * 4 + (col >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      vrd[dt] = static_cast<uint32_t>(rr * ROWB + (((dt * 2 + ((col & 3) >> 1)) ^ chunk_swz<D>(rr)) % NCH) * 16 +
+                                      (col & 1) * 8);
+  }
+
+  // S^T tile from K rows in LDS
+  auto qk = [&](const uint16_t* kt_lds, f32x4_t (&s)[4][2]) {
+    const char* kb = reinterpret_cast<const char*>(kt_lds);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) s[kt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const bf16x8_t ka = as_bf16x8(*reinterpret_cast<const Vec16*>(kb + krd[ks] + kt * 16 * ROWB));
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          s[kt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qop[t][ks], s[kt][t], 0, 0, 0);
+      }
+    }
+  };
+
+  f32x4_t o[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) o[dt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY};
+  float l[2] = {0.f, 0.f};
+
+  issue(k_cache, k_stride_bytes, kload, lds_k[0], 0);
+  issue(v_cache, v_stride_bytes, vload, lds_v[0], 0);
+  if (nkt > 1) issue(k_cache, k_stride_bytes, kload, lds_k[1], kKeys);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x4_t s_cur[4][2];
+  qk(sK[0], s_cur);
+
+  // running-max helpers: masking of a tile that crosses the diagonal or the
+  // key end; the tile max in eight pieces (so it can be spread over MFMAs);
+  // and the lazy move of the reference max (O and l rescaled), which must
+  // come after every P V product that used the old max
+  auto mask_tile = [&](f32x4_t (&sx)[4][2], int kt0) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int lim = min(posq[t], Lk - 1) - (kt0 + gq * 4);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sx[kt][t][e] = (kt * 16 + e <= lim) ? sx[kt][t][e] : -INFINITY;
+    }
+  };
+  float tm[2], mc[2];
+  auto max_piece = [&](int c, const f32x4_t (&sx)[4][2]) {
+    const int t = c / 4;
+    switch (c % 4) {
+      case 0:
+        tm[t] = max3f(sx[0][t][0], sx[0][t][1], sx[0][t][2]);
+        tm[t] = max3f(tm[t], sx[0][t][3], sx[1][t][0]);
+        break;
+      case 1:
+        tm[t] = max3f(tm[t], sx[1][t][1], sx[1][t][2]);
+        tm[t] = max3f(tm[t], sx[1][t][3], sx[2][t][0]);
+        break;
+      case 2:
+        tm[t] = max3f(tm[t], sx[2][t][1], sx[2][t][2]);
+        tm[t] = max3f(tm[t], sx[2][t][3], sx[3][t][0]);
+        tm[t] = max3f(tm[t], sx[3][t][1], sx[3][t][2]);
+        tm[t] = max2f(tm[t], sx[3][t][3]);
+        break;
+      default:
+        mc[t] = col_max(tm[t]) * scale_log2;
+        break;
+    }
+  };
+  auto move_max = [&]() {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (__any(mc[t] > m[t] + kMaxSlack)) {
+        const float m_new = max2f(m[t], mc[t]);
+        const float alpha = fast_exp2(m[t] - m_new);
+        l[t] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt][t] *= alpha;
+        m[t] = m_new;
+      }
+    }
+  };
+  auto need_mask_at = [&](int kt0) { return !(kt0 + kKeys - 1 <= start + q_lo && kt0 + kKeys <= Lk); };
+
+  if (need_mask_at(0)) mask_tile(s_cur, 0);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) max_piece(c, s_cur);
+  move_max();
+
+  for (int j = 0; j < nkt; ++j) {
+    const int kt0 = j * kKeys;
+    // everything issued in the previous iteration has landed, and every wave
+    // is done with K(j) (read for S(j) one iteration ago) and V(j - 1)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j + 2 < nkt) issue(k_cache, k_stride_bytes, kload, lds_k[j & 1], kt0 + 2 * kKeys);
+    if (j + 1 < nkt) issue(v_cache, v_stride_bytes, vload, lds_v[(j + 1) & 1], kt0 + kKeys);
+
+    f32x4_t s_next[4][2];
+    Vec16 pop[2][2];
+    // S(j+1) = K(j+1) Q^T on the matrix cores, interleaved by hand with this
+    // tile's exp2 / packing / row sums on the vector ALU: after every MFMA,
+    // three of the 96 vector instructions; K operands are read one k-step
+    // ahead. (On the last tile the K buffer is stale; those scores are never
+    // used.) A scheduling fence after each slot keeps the order.
+    {
+      const char* kb = reinterpret_cast<const char*>(sK[(j + 1) & 1]);
+      bf16x8_t kop[2][4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) kop[0][kt] = as_bf16x8(*reinterpret_cast<const Vec16*>(kb + krd[0] + kt * 16 * ROWB));
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) s_next[kt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      float lsum[2] = {l[0], l[1]};
+      auto vop = [&](int k) {
+        const int t = k / 48;
+        const int r = k % 48;
+        if (r < 32) {
+          const int el = r / 2;
+          const int kt = el / 4, e = el % 4;
+          if ((r & 1) == 0) s_cur[kt][t][e] = fmaf(s_cur[kt][t][e], scale_log2, -m[t]);
+          else s_cur[kt][t][e] = fast_exp2(s_cur[kt][t][e]);
+        } else if (r < 40) {
+          const int q = r - 32, st = q / 4, w = q % 4;
+          const int kt = 2 * st + w / 2, e0 = 2 * (w % 2);
+          pop[st][t].w[w] = pack2(s_cur[kt][t][e0], s_cur[kt][t][e0 + 1]);
+        } else {
+          const int q = r - 40, st = q / 4, w = q % 4;
+          lsum[t] = dot2_bf16(pop[st][t].w[w], kOnesBf16x2, lsum[t]);
+        }
+      };
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+            kop[(ks + 1) & 1][kt] = as_bf16x8(*reinterpret_cast<const Vec16*>(kb + krd[ks + 1] + kt * 16 * ROWB));
+        }
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int i = (ks * 4 + kt) * 2 + t;
+            s_next[kt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks & 1][kt], qop[t][ks], s_next[kt][t], 0, 0, 0);
+            constexpr int PER_MFMA = 96 / (KS * 8);
+#pragma unroll
+            for (int u = 0; u < PER_MFMA; ++u) vop(PER_MFMA * i + u);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      }
+      l[0] = lsum[0];
+      l[1] = lsum[1];
+      // keep the weights computed here, beside the MFMAs (the compiler would
+      // otherwise sink them past the masking branch below)
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          asm volatile("" :: "v"(pop[st][t].w[0]), "v"(pop[st][t].w[1]), "v"(pop[st][t].w[2]), "v"(pop[st][t].w[3]));
+      asm volatile("" :: "v"(l[0]), "v"(l[1]));
+    }
+    const bool has_next = j + 1 < nkt;
+    if (has_next && need_mask_at(kt0 + kKeys)) mask_tile(s_next, kt0 + kKeys);
+
+    // O^T += V^T P^T, interleaved with the next tile's max (eight pieces);
+    // lane (gq, col) takes column dt * 16 + col of the keys st * 32 + gq * 4
+    // + 0..3 and st * 32 + 16 + gq * 4 + 0..3 (the order in which the P^T
+    // operand holds them); V operands are read one head_dim tile ahead
+    {
+      const char* vt = reinterpret_cast<const char*>(sV[j & 1]);
+      s16x4_t va[2][2][2];
+      auto vread = [&](int dt, int bufi) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          va[bufi][st][0] = ds_read_tr16(reinterpret_cast<const uint16_t*>(vt + vrd[dt] + st * 32 * ROWB));
+          va[bufi][st][1] = ds_read_tr16(reinterpret_cast<const uint16_t*>(vt + vrd[dt] + (st * 32 + 16) * ROWB));
+        }
+      };
+      vread(0, 0);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        if (dt + 1 < DT) vread(dt + 1, (dt + 1) & 1);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const s16x4_t lo = va[dt & 1][st][0];
+          const s16x4_t hi = va[dt & 1][st][1];
+          const bf16x8_t a = __builtin_bit_cast(
+              bf16x8_t, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int i = (dt * 2 + st) * 2 + t;
+            o[dt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pop[st][t]), o[dt][t], 0, 0, 0);
+            constexpr int EVERY = (DT * 4) / 8;
+            if (i % EVERY == EVERY - 1) max_piece(i / EVERY, s_next);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    }
+    if (has_next) move_max();
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) s_cur[kt][t] = s_next[kt][t];
+  }
+
+  write_out<D>(out, o, l, orow, ohead, num_q_heads, gq, 1.f);
+}
+
 template <int D, int G, bool FP8>
 hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
   constexpr int KB = FP8 ? 1 : 2;
@@ -537,6 +920,15 @@ hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
   dim3 grid(static_cast<uint32_t>(total));
   // an E4M3 cache holds K / k_scale: the score scale absorbs k_scale
   const float scale_log2 = a.scale * (FP8 ? a.k_scale : 1.f) * kLog2e;
+  const bool whole_rows = a.block_tables == nullptr || log2_bs >= 6;
+  if (!FP8 && whole_rows) {
+    hipLaunchKernelGGL((prefill_direct_kernel<D, G>), grid, dim3(kThreads), 0, stream,
+                       static_cast<uint16_t*>(a.out), static_cast<const char*>(a.q), a.q_stride * 2,
+                       static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache),
+                       a.k_stride * KB, a.v_stride * KB, a.cu_q, a.cu_k, a.block_tables, a.max_blocks,
+                       a.num_q_heads, a.num_kv_heads, log2_bs, scale_log2, max_qt);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((prefill_kernel<D, G, FP8>), grid, dim3(kThreads), 0, stream,
                      static_cast<uint16_t*>(a.out), static_cast<const char*>(a.q), a.q_stride * 2,
                      static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache),
