@@ -592,24 +592,39 @@ hipError_t dispatch_fused(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 int32_t decode_partition_tokens(int32_t requested, int32_t num_seqs, int32_t num_kv_heads,
-                                int32_t group, int32_t block_size, int32_t max_blocks) {
+                                int32_t group, int32_t block_size, int32_t max_blocks,
+                                int32_t elem_bytes) {
   if (requested > 0) return requested;
   const int64_t max_ctx = static_cast<int64_t>(max_blocks) * block_size;
-  // Short histories: one pass, no merge launch (the launch latency of a
-  // second kernel costs more than the parallelism it would buy).
-  const int64_t one_pass = (max_ctx + 63) / 64 * 64;
-  if (one_pass <= 1024 && static_cast<int64_t>(group) * one_pass <= 8192)
-    return static_cast<int32_t>(one_pass);
-  // Longest partition (fewest partials to merge) that still gives the grid
-  // enough workgroups to cover the chip several times when every sequence
-  // is as long as its table allows; the LDS score buffer caps group * length.
-  const int64_t want = 8192;
-  for (int32_t part : {1024, 512}) {
-    if (static_cast<int64_t>(group) * part > 8192) continue;
-    const int64_t wgs = static_cast<int64_t>(num_seqs) * num_kv_heads * ((max_ctx + part - 1) / part);
-    if (wgs >= want) return part;
-  }
-  return 256;
+  const int64_t heads = static_cast<int64_t>(num_seqs) * num_kv_heads;
+  auto fits = [&](int64_t part) { return static_cast<int64_t>(group) * part <= 8192; };  // LDS scores
+  auto wgs = [&](int64_t part) { return heads * ((max_ctx + part - 1) / part); };
+  // stretch = tokens per byte relative to a 16-bit cache
+  auto rule = [&](int64_t stretch) -> int64_t {
+    // Short histories over a grid that already fills the chip: one pass, no
+    // merge launch (its latency costs more than the parallelism it would buy).
+    const int64_t one_pass = (max_ctx + 63) / 64 * 64;
+    if (one_pass <= 1024 * stretch && fits(one_pass) && heads >= 512) return one_pass;
+    // Longest partition (fewest partials to merge) that still gives the grid
+    // enough workgroups to cover the chip several times when every sequence
+    // is as long as its table allows.
+    for (int64_t part : {1024, 512}) {
+      part *= stretch;
+      if (fits(part) && wgs(part) >= 8192) return part;
+    }
+    int64_t part = fits(256 * stretch) ? 256 * stretch : 256;
+    // Small grids are latency-bound: cut the history finer, to about 512
+    // workgroups, but not below 64 tokens.
+    if (wgs(part) < 512) {
+      const int64_t fine = (max_ctx * heads + 511) / 512;
+      part = fine <= 64 ? 64 : (fine + 63) / 64 * 64;
+      if (part > 256 * stretch) part = 256 * stretch;
+    }
+    return part;
+  };
+  const int64_t part16 = rule(1);
+  const int64_t part = elem_bytes == 1 ? (rule(2) > part16 ? rule(2) : part16) : part16;
+  return static_cast<int32_t>(part);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

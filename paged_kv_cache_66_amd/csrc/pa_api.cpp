@@ -44,11 +44,11 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Partition length for a decode call, or -1 when the request is invalid.
 int32_t resolve_partition(int32_t requested, int32_t num_seqs, int32_t num_kv_heads, int32_t group,
-                          int32_t block_size, int32_t max_blocks) {
+                          int32_t block_size, int32_t max_blocks, int32_t elem_bytes) {
   if (requested < 0) return -1;
   if (requested > 0 && (requested % 64 != 0 || requested > kMaxPartition)) return -1;
   return pa::decode_partition_tokens(requested, num_seqs, num_kv_heads, group, block_size,
-                                     max_blocks);
+                                     max_blocks, elem_bytes);
 }
 
 int64_t num_partitions(int32_t partition, int32_t block_size, int32_t max_blocks) {
@@ -102,7 +102,8 @@ pa_status prepare_decode(void* out, const void* q, int64_t q_row_stride, const v
   if (st != PA_OK) return st;
   if (!scale_ok(scale)) return PA_ERR_SHAPE;
   const int32_t part = resolve_partition(partition_size, num_seqs, num_kv_heads, G, block_size,
-                                         max_blocks_per_seq);
+                                         max_blocks_per_seq,
+                                         kv == pa::KvFormat::kFp8E4m3 ? 1 : kv == pa::KvFormat::kF32 ? 4 : 2);
   if (part <= 0) return PA_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(G) * part > kMaxScoreWords) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
@@ -304,8 +305,9 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
       head_dim <= 0 || !is_pow2(block_size) || max_blocks_per_seq <= 0)
     return 0;
+  // sized for 16-bit caches: no cache format takes more partitions
   const int32_t part = resolve_partition(partition_size, num_seqs, num_kv_heads,
-                                         num_q_heads / num_kv_heads, block_size, max_blocks_per_seq);
+                                         num_q_heads / num_kv_heads, block_size, max_blocks_per_seq, 2);
   if (part <= 0) return 0;
   const int64_t P = num_partitions(part, block_size, max_blocks_per_seq);
   if (P <= 1) return 0;

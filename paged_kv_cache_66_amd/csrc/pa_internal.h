@@ -91,8 +91,13 @@ struct PrefillArgs {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 // Partition sizing shared by pa_decode and pa_decode_workspace_size
-// (requested > 0 is returned as is; 0 picks the default for the shape).
+// (requested > 0 is returned as is; 0 picks the default for the shape and
+// the cache element size: a one-byte cache takes partitions twice as long,
+// so a workgroup still streams as many bytes). The default never shortens
+// when elem_bytes shrinks, so sizing a workspace with elem_bytes = 2 covers
+// every cache format.
 int32_t decode_partition_tokens(int32_t requested, int32_t num_seqs, int32_t num_kv_heads,
-                                int32_t group, int32_t block_size, int32_t max_blocks);
+                                int32_t group, int32_t block_size, int32_t max_blocks,
+                                int32_t elem_bytes);
 
 }  // namespace pa

@@ -97,9 +97,10 @@ def test_decode_validation(lib):
     assert decode(lib, scale=-0.5) == SHAPE
     # W * bs = 64 fits the default partition: single pass, no workspace needed
     assert lib.pa_decode_workspace_size(4, 4, 2, 64, 16, 4, 0) == 0
-    # W * bs = 2048 with few sequences -> default partition 256: 8 partials
+    # W * bs = 2048 over a grid of 8 (sequence, kv head) pairs: the default
+    # cuts it into 64-token partitions (about 512 workgroups): 32 partials
     need = lib.pa_decode_workspace_size(4, 4, 2, 64, 16, 128, 0)
-    assert need == 4 * 4 * 8 * (64 + 2) * 4
+    assert need == 4 * 4 * 32 * (64 + 2) * 4
     # an explicit partition of 512 -> 4 partials
     assert lib.pa_decode_workspace_size(4, 4, 2, 64, 16, 128, 512) == 4 * 4 * 4 * (64 + 2) * 4
     assert lib.pa_decode_workspace_size(4, 4, 3, 64, 16, 128, 0) == 0  # invalid group
