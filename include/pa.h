@@ -114,7 +114,10 @@ pa_status pa_store_kvcache(const void* key, int64_t key_row_stride,
  * pa_decode_workspace_size - bytes of device workspace pa_decode needs for
  * these sizes (0 when the call runs as a single pass, or when the sizes are
  * invalid). partition_size is the same value later passed to pa_decode
- * (0 = library default, which depends on the launch shape).
+ * (0 = library default, which depends on the launch shape and the cache
+ * element size). The size is computed for 16-bit caches; the default for an
+ * fp8 cache is never a shorter partition, so the same size serves the *_fp8
+ * decode calls, and those calls require it.
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
