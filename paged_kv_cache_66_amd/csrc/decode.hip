@@ -202,6 +202,12 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   // vectors each (fewer lanes per row -> fewer reduction steps)
   constexpr int LPT1 = D / (2 * EPV);
   constexpr int TPW1 = 64 / LPT1;
+  // 8-byte vectors (E4M3): a lane's two vectors are adjacent and travel as
+  // one 16-byte load, so a load instruction takes 128 contiguous bytes of
+  // each row; 16-byte vectors take the row in two halves
+  constexpr bool kPair = VB == 8;
+  constexpr int kSecond = kPair ? VB : LPT1 * VB;    // byte offset of the second vector
+  constexpr int kFirst = kPair ? 2 * VB : VB;        // bytes between lanes' first vectors
   constexpr int STEP1 = kWaves * TPW1;
   // value pass: LPT lanes per row, one vector each (fewer accumulators)
   constexpr int LPT = D / EPV;       // lanes per (token, kv head) row
@@ -303,7 +309,7 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const char* qh = qrow + static_cast<int64_t>(g * G + h) * D * QB;
-      qs[h].load(load16(qh + li1 * EPV * QB), load16(qh + (LPT1 + li1) * EPV * QB));
+      qs[h].load(load16(qh + (li1 * kFirst / VB) * EPV * QB), load16(qh + (li1 * kFirst + kSecond) / VB * EPV * QB));
     }
   }
   __syncthreads();
@@ -323,7 +329,7 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   const int nloop = new_tl >= 0 ? ntok - 1 : ntok;  // rows read from the cache
 
   // phase 1: raw scores q . k (the scale is applied once per score in phase 2)
-  const char* kbase1 = k_cache + static_cast<int64_t>(g) * D * EB + li1 * VB;
+  const char* kbase1 = k_cache + static_cast<int64_t>(g) * D * EB + li1 * kFirst;
   const int my_row1 = wave * TPW1 + grp1;
   for (int base = 0; base < nloop; base += STEP1 * kUnroll) {
     Vec k0[kUnroll], k1[kUnroll];
@@ -332,8 +338,14 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
       const int tl = base + u * STEP1 + my_row1;
       if (tl < nloop) {
         const char* r = kbase1 + row_off(tl);
-        k0[u] = E::load_nt(r);
-        k1[u] = E::load_nt(r + LPT1 * VB);
+        if constexpr (kPair) {
+          const Vec16 both = load16_nt(r);
+          k0[u] = Vec{{both.w[0], both.w[1]}};
+          k1[u] = Vec{{both.w[2], both.w[3]}};
+        } else {
+          k0[u] = E::load_nt(r);
+          k1[u] = E::load_nt(r + kSecond);
+        }
       } else {
         k0[u] = Vec{};
         k1[u] = Vec{};
@@ -353,8 +365,8 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   }
   if constexpr (FUSED) {
     if (new_tl >= 0) {  // uniform: every lane joins the row-group sums
-      const Vec nk0 = *reinterpret_cast<const Vec*>(s_new + li1 * VB);
-      const Vec nk1 = *reinterpret_cast<const Vec*>(s_new + (LPT1 + li1) * VB);
+      const Vec nk0 = *reinterpret_cast<const Vec*>(s_new + li1 * kFirst);
+      const Vec nk1 = *reinterpret_cast<const Vec*>(s_new + li1 * kFirst + kSecond);
       float sc[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) sc[h] = group_sum<LPT1>(qs[h].dot(nk0, nk1));
