@@ -241,6 +241,44 @@ pa_status pa_prefill_varlen(void* out, const void* q, int64_t q_row_stride, int3
                             int32_t num_blocks, float scale, pa_dtype dtype, void* stream);
 
 /*
+ * pa_store_prefill - the prefill step's scatter and attention in one launch
+ * (the two calls of Attention.forward in prefill with a block table:
+ * "Inference Engine Inside nano-vLLM", "Attention in nano-vLLM":
+ * store_kvcache, then flash_attn_varlen_func over the caches; "nano-vLLM
+ * Part 2 ...", sections 2.3 and 4.1).
+ *
+ * Same result, bit for bit (out and both caches), as pa_store_kvcache(key,
+ * value, k_cache, v_cache, slot_mapping, total_q tokens) followed by
+ * pa_prefill_varlen(...) in paged mode with the same arguments, when:
+ *   - slot_mapping[cu_seqlens_q[i] + j] is the slot that sequence i's
+ *     block-table row gives position Lk - Lq + j (as the prefill runner
+ *     builds it), for every sequence i and 0 <= j < Lq;
+ *   - no slot written is also a prefix slot (position < Lk - Lq) of any
+ *     sequence of the call.
+ * Keys at positions Lk - Lq .. Lk - 1 are read from key / value (the
+ * workgroup that owns a query row writes that row's K / V to the caches);
+ * only the cached prefix is read from the caches. A slot of -1 stores
+ * nothing; its row is still attended to from key / value.
+ *
+ *   key, value    [total_q, num_kv_heads, head_dim] bf16; row r at
+ *                 key + r * key_row_stride (elements, rows 16-byte aligned).
+ *   slot_mapping  int32 [total_q], device.
+ *   k_cache, v_cache  [num_blocks, block_size, num_kv_heads, head_dim];
+ *                 written at the slots, otherwise read only.
+ *   block_tables  must not be NULL (PA_ERR_NULL), nor slot_mapping.
+ * Everything else as pa_prefill_varlen in paged mode, including the error
+ * codes; only PA_BF16.
+ */
+pa_status pa_store_prefill(void* out, const void* q, int64_t q_row_stride, int32_t total_q,
+                           const void* key, int64_t key_row_stride, const void* value,
+                           int64_t value_row_stride, const int32_t* slot_mapping, void* k_cache,
+                           void* v_cache, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                           int32_t max_seqlen_q, int32_t max_seqlen_k, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, float scale, pa_dtype dtype, void* stream);
+
+/*
  * ---------------------------------------------------------------------------
  * fp8 KV caches
  * ---------------------------------------------------------------------------
@@ -310,6 +348,21 @@ pa_status pa_prefill_varlen_fp8(void* out, const void* q, int64_t q_row_stride, 
                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                 float scale, float k_scale, float v_scale, pa_dtype dtype,
                                 void* stream);
+
+/* pa_store_prefill over fp8 caches: bit for bit pa_store_kvcache_fp8 then
+ * pa_prefill_varlen_fp8 with the same arguments (same preconditions as
+ * pa_store_prefill); this step's keys and values enter the attention as their
+ * E4M3 codes, exactly as the caches hold them. */
+pa_status pa_store_prefill_fp8(void* out, const void* q, int64_t q_row_stride, int32_t total_q,
+                               const void* key, int64_t key_row_stride, const void* value,
+                               int64_t value_row_stride, const int32_t* slot_mapping,
+                               void* k_cache, void* v_cache, const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_k, int32_t max_seqlen_q,
+                               int32_t max_seqlen_k, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, float scale, float k_scale, float v_scale,
+                               pa_dtype dtype, void* stream);
 
 #ifdef __cplusplus
 }

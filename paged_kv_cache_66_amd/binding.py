@@ -55,6 +55,12 @@ _SIGNATURES = {
     "pa_prefill_varlen_fp8": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
                                              _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32,
                                              _f32, ctypes.c_int, _vp]),
+    "pa_store_prefill": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp,
+                                        _vp, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                        _f32, ctypes.c_int, _vp]),
+    "pa_store_prefill_fp8": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _i64, _vp, _i64, _vp, _vp, _vp,
+                                            _vp, _vp, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                            _i32, _f32, _f32, _f32, ctypes.c_int, _vp]),
 }
 
 
@@ -375,4 +381,60 @@ def pa_prefill_varlen_fp8(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, max_s
                                    bsq, hq, hkv, d, bs, n, float(scale), float(k_scale), float(v_scale),
                                    PA_BF16, _stream(q))
     _check("pa_prefill_varlen_fp8", st)
+    return out
+
+
+def _store_prefill_args(q, key, value, slot_mapping, cu_seqlens_q, cu_seqlens_k, block_tables, dims, out):
+    import torch
+    n, bs, hkv, d = dims
+    for t, name in ((cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k"),
+                    (block_tables, "block_tables"), (slot_mapping, "slot_mapping")):
+        _int32(t, name)
+    qp, qs = _rows(q, "q")
+    kp, ks = _rows(key, "key")
+    vp, vs = _rows(value, "value")
+    tq, hq = int(q.shape[0]), int(q.shape[1])
+    bsq = int(cu_seqlens_q.shape[0]) - 1
+    _require(cu_seqlens_k.shape == cu_seqlens_q.shape, "cu_seqlens_k must match cu_seqlens_q")
+    _require(block_tables.dim() == 2 and block_tables.shape[0] == bsq, "block_tables must be [B, W]")
+    _require(q.shape[2] == d and q.dtype == torch.bfloat16, "q shape/dtype")
+    _require(tuple(key.shape) == (tq, hkv, d) and tuple(value.shape) == (tq, hkv, d), "key/value shape")
+    _require(key.dtype == value.dtype == torch.bfloat16, "key/value must be bf16")
+    _require(slot_mapping.shape == (tq,), "slot_mapping must be [Tq]")
+    if out is None:
+        out = torch.empty((tq, hq, d), dtype=q.dtype, device=q.device)
+    _require(out.is_contiguous() and tuple(out.shape) == (tq, hq, d) and out.dtype == q.dtype, "out")
+    return out, [out.data_ptr(), qp, qs, tq, kp, ks, vp, vs, slot_mapping.data_ptr()], \
+        [cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr()], \
+        [block_tables.data_ptr(), int(block_tables.shape[1]), bsq, hq, hkv, d, bs, n]
+
+
+def pa_store_prefill(q, key, value, slot_mapping, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k,
+                     max_seqlen_q, max_seqlen_k, block_tables, scale, out=None):
+    """pa_store_kvcache + paged pa_prefill_varlen in one launch. q [Tq, H_q, D];
+    key/value [Tq, H_kv, D] are this step's rows, packed like q;
+    slot_mapping[r] is the slot of query row r's position."""
+    lib = load()
+    dims = _cache_dims(k_cache, v_cache)
+    _require(k_cache.dtype == q.dtype, "caches must be bf16 like q")
+    out, a, cu, t = _store_prefill_args(q, key, value, slot_mapping, cu_seqlens_q, cu_seqlens_k,
+                                        block_tables, dims, out)
+    st = lib.pa_store_prefill(*a, k_cache.data_ptr(), v_cache.data_ptr(), *cu, int(max_seqlen_q),
+                              int(max_seqlen_k), *t, float(scale), PA_BF16, _stream(q))
+    _check("pa_store_prefill", st)
+    return out
+
+
+def pa_store_prefill_fp8(q, key, value, slot_mapping, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k,
+                         max_seqlen_q, max_seqlen_k, block_tables, scale, k_scale, v_scale, out=None):
+    """pa_store_kvcache_fp8 + pa_prefill_varlen_fp8 in one launch (same
+    arguments as pa_store_prefill plus the two cache scales)."""
+    lib = load()
+    dims = _fp8_cache_dims(k_cache, v_cache)
+    out, a, cu, t = _store_prefill_args(q, key, value, slot_mapping, cu_seqlens_q, cu_seqlens_k,
+                                        block_tables, dims, out)
+    st = lib.pa_store_prefill_fp8(*a, k_cache.data_ptr(), v_cache.data_ptr(), *cu, int(max_seqlen_q),
+                                  int(max_seqlen_k), *t, float(scale), float(k_scale), float(v_scale),
+                                  PA_BF16, _stream(q))
+    _check("pa_store_prefill_fp8", st)
     return out

@@ -194,7 +194,9 @@ pa_status prefill_common(void* out, const void* q, int64_t q_row_stride, int32_t
                          int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                          int32_t num_blocks, float scale, pa_dtype dtype, bool fp8, float k_scale,
-                         float v_scale, void* stream) {
+                         float v_scale, void* stream, const void* new_k = nullptr,
+                         int64_t new_k_stride = 0, const void* new_v = nullptr,
+                         int64_t new_v_stride = 0, const int32_t* slot_mapping = nullptr) {
   if (dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   if (!scale_ok(k_scale) || !scale_ok(v_scale)) return PA_ERR_SHAPE;
   if (total_q < 0 || num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_q_heads <= 0 ||
@@ -230,6 +232,12 @@ pa_status prefill_common(void* out, const void* q, int64_t q_row_stride, int32_t
   if (!aligned16(out) || !aligned16(k) || !aligned16(v)) return PA_ERR_ALIGN;
   if ((st = check_rows(q, q_row_stride, static_cast<int64_t>(num_q_heads) * head_dim, eb)) != PA_OK)
     return st;
+  const bool fused = slot_mapping != nullptr;
+  if (fused) {
+    if (new_k == nullptr || new_v == nullptr) return PA_ERR_NULL;
+    if ((st = check_rows(new_k, new_k_stride, row, eb)) != PA_OK) return st;
+    if ((st = check_rows(new_v, new_v_stride, row, eb)) != PA_OK) return st;
+  }
   pa::PrefillArgs a{};
   a.out = out;
   a.q = q;
@@ -254,6 +262,13 @@ pa_status prefill_common(void* out, const void* q, int64_t q_row_stride, int32_t
   a.fp8 = fp8;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  if (fused) {
+    a.new_k = new_k;
+    a.new_k_stride = new_k_stride;
+    a.new_v = new_v;
+    a.new_v_stride = new_v_stride;
+    a.slot_mapping = slot_mapping;
+  }
   return pa::launch_prefill(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -404,6 +419,41 @@ pa_status pa_prefill_varlen_fp8(void* out, const void* q, int64_t q_row_stride, 
                         cu_seqlens_k, max_seqlen_q, max_seqlen_k, block_tables,
                         max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim,
                         block_size, num_blocks, scale, dtype, true, k_scale, v_scale, stream);
+}
+
+pa_status pa_store_prefill(void* out, const void* q, int64_t q_row_stride, int32_t total_q,
+                           const void* key, int64_t key_row_stride, const void* value,
+                           int64_t value_row_stride, const int32_t* slot_mapping, void* k_cache,
+                           void* v_cache, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                           int32_t max_seqlen_q, int32_t max_seqlen_k, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, float scale, pa_dtype dtype, void* stream) {
+  if (dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (block_tables == nullptr || slot_mapping == nullptr) return PA_ERR_NULL;
+  return prefill_common(out, q, q_row_stride, total_q, k_cache, 0, v_cache, 0, cu_seqlens_q,
+                        cu_seqlens_k, max_seqlen_q, max_seqlen_k, block_tables,
+                        max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                        block_size, num_blocks, scale, dtype, false, 1.f, 1.f, stream, key,
+                        key_row_stride, value, value_row_stride, slot_mapping);
+}
+
+pa_status pa_store_prefill_fp8(void* out, const void* q, int64_t q_row_stride, int32_t total_q,
+                               const void* key, int64_t key_row_stride, const void* value,
+                               int64_t value_row_stride, const int32_t* slot_mapping,
+                               void* k_cache, void* v_cache, const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_k, int32_t max_seqlen_q,
+                               int32_t max_seqlen_k, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, float scale, float k_scale, float v_scale,
+                               pa_dtype dtype, void* stream) {
+  if (block_tables == nullptr || slot_mapping == nullptr) return PA_ERR_NULL;
+  return prefill_common(out, q, q_row_stride, total_q, k_cache, 0, v_cache, 0, cu_seqlens_q,
+                        cu_seqlens_k, max_seqlen_q, max_seqlen_k, block_tables,
+                        max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                        block_size, num_blocks, scale, dtype, true, k_scale, v_scale, stream, key,
+                        key_row_stride, value, value_row_stride, slot_mapping);
 }
 
 }  // extern "C"

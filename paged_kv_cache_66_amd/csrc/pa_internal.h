@@ -86,6 +86,15 @@ struct PrefillArgs {
   bool fp8;       // paged E4M3 caches (bf16 queries and outputs)
   float k_scale;
   float v_scale;
+  // fused store (slot_mapping != nullptr): this step's new K/V rows, packed
+  // like q (row cu_q[i] + j is position Lk - Lq + j of sequence i), are
+  // written to the caches at slot_mapping[row] and read from here, never
+  // from the caches, by the attention of the same launch
+  const void* new_k;
+  const void* new_v;
+  int64_t new_k_stride;  // elements
+  int64_t new_v_stride;
+  const int32_t* slot_mapping;
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

@@ -328,13 +328,48 @@ template <> struct TileVec<true> {
   }
 };
 
-template <int D, int G, bool FP8>
+
+// Fused store: the query rows of this workgroup are this step's new tokens.
+// Their K and V rows of kv head g (8-element chunks, packed rows of new_k /
+// new_v) go to the cache slots slot_mapping[row] (E4M3 caches: quantised with
+// k_scale / v_scale, as pa_store_kvcache_fp8 does); slot -1 stores nothing.
+// Every (row, kv head) pair belongs to exactly one workgroup.
+template <int D, bool FP8>
+__device__ __forceinline__ void store_new_rows(char* __restrict__ k_cache, char* __restrict__ v_cache,
+                                               int64_t cache_row_bytes, const char* __restrict__ new_k,
+                                               const char* __restrict__ new_v, int64_t nk_stride_bytes,
+                                               int64_t nv_stride_bytes, const int32_t* __restrict__ slot_mapping,
+                                               int row0, int nrows, int g, float k_scale, float v_scale) {
+  constexpr int CH = D / 8;  // 8-element chunks per head slice
+  const int n = nrows * 2 * CH;
+  for (int idx = threadIdx.x; idx < n; idx += blockDim.x) {
+    const int c = idx % CH;
+    const int rv = idx / CH;
+    const bool is_v = rv & 1;
+    const int r = row0 + (rv >> 1);
+    const int slot = slot_mapping[r];
+    if (slot < 0) continue;
+    const Vec16 x = load16((is_v ? new_v + r * nv_stride_bytes : new_k + r * nk_stride_bytes) +
+                           (static_cast<int64_t>(g) * D + c * 8) * 2);
+    char* dst = (is_v ? v_cache : k_cache) + static_cast<int64_t>(slot) * cache_row_bytes +
+                (static_cast<int64_t>(g) * D + c * 8) * (FP8 ? 1 : 2);
+    if constexpr (FP8) {
+      store8(dst, quantize8(x, is_v ? v_scale : k_scale));
+    } else {
+      store16(dst, x);
+    }
+  }
+}
+
+template <int D, int G, bool FP8, bool FUSED>
 __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
     uint16_t* __restrict__ out, const char* __restrict__ q, int64_t q_stride_bytes,
     const char* __restrict__ k_cache, const char* __restrict__ v_cache, int64_t k_stride_bytes,
     int64_t v_stride_bytes, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
     const int32_t* __restrict__ block_tables, int32_t max_blocks, int32_t num_q_heads,
-    int32_t num_kv_heads, int32_t log2_bs, float scale_log2, int32_t max_qt, float v_scale) {
+    int32_t num_kv_heads, int32_t log2_bs, float scale_log2, int32_t max_qt, float v_scale,
+    const char* __restrict__ new_k, const char* __restrict__ new_v, int64_t nk_stride_bytes,
+    int64_t nv_stride_bytes, const int32_t* __restrict__ slot_mapping, float k_scale) {
   using TV = TileVec<FP8>;
   using KVec = typename TV::Vec;
   constexpr int KB = FP8 ? 1 : 2;  // bytes per cache element
@@ -378,6 +413,10 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   int orow[2];   // packed query row, -1 when this column is padding
   int ohead[2];
   load_q<D, G>(q, q_stride_bytes, q0, Lq, q_lo, start, g, wave, col, gq, qop, posq, orow, ohead);
+  if constexpr (FUSED)
+    store_new_rows<D, FP8>(const_cast<char*>(k_cache), const_cast<char*>(v_cache), k_stride_bytes, new_k, new_v,
+                           nk_stride_bytes, nv_stride_bytes, slot_mapping, q0 + q_lo, q_hi - q_lo, g, k_scale,
+                           v_scale);
 
   // Key rows come either from the paged caches (row stride H_kv * D) through
   // the block table, or, without a table, from packed k / v tensors where key
@@ -416,6 +455,39 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   }
 
   auto fetch = [&](int kt0) {
+    if constexpr (FUSED) {
+      // keys at or after `start` are this step's rows: read them from new_k
+      // / new_v (E4M3: quantised as the store does), never from the caches
+      if (kt0 + kKeys > start) {
+#pragma unroll
+        for (int u = 0; u < KLOADS; ++u) {
+          const int item = tid + u * kThreads;
+          const int key = kt0 + item / KCH;
+          const int c = item % KCH;
+          if (key >= Lk) {
+            kreg[u] = KVec{};
+            vreg[u] = KVec{};
+          } else if (key < start) {
+            const int64_t ra = row_addr(key) + c * CB;
+            kreg[u] = TV::load(k_cache + ra);
+            vreg[u] = TV::load(v_cache + ra);
+          } else {
+            const int64_t r = q0 + key - start;
+            const int64_t ho = (static_cast<int64_t>(g) * D + c * 8) * 2;
+            const Vec16 kx = load16(new_k + r * nk_stride_bytes + ho);
+            const Vec16 vx = load16(new_v + r * nv_stride_bytes + ho);
+            if constexpr (FP8) {
+              kreg[u] = quantize8(kx, k_scale);
+              vreg[u] = quantize8(vx, v_scale);
+            } else {
+              kreg[u] = kx;
+              vreg[u] = vx;
+            }
+          }
+        }
+        return;
+      }
+    }
     if (tile_contiguous) {
       // kt0 < Lk always, so the tile's first row exists
       const char* kb = paged ? k_cache + row_addr(kt0) : k_cache + (k0_row + kt0) * k_stride_bytes + head_off;
@@ -556,13 +628,15 @@ __device__ __forceinline__ int chunk_swz(int r) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <int D, int G>
+template <int D, int G, bool FUSED>
 __global__ void __launch_bounds__(kThreads, 2) prefill_direct_kernel(
     uint16_t* __restrict__ out, const char* __restrict__ q, int64_t q_stride_bytes,
     const char* __restrict__ k_cache, const char* __restrict__ v_cache, int64_t k_stride_bytes,
     int64_t v_stride_bytes, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
     const int32_t* __restrict__ block_tables, int32_t max_blocks, int32_t num_q_heads,
-    int32_t num_kv_heads, int32_t log2_bs, float scale_log2, int32_t max_qt) {
+    int32_t num_kv_heads, int32_t log2_bs, float scale_log2, int32_t max_qt,
+    const char* __restrict__ new_k, const char* __restrict__ new_v, int64_t nk_stride_bytes,
+    int64_t nv_stride_bytes, const int32_t* __restrict__ slot_mapping) {
   constexpr int QT = kRows / G;      // queries per workgroup
   constexpr int KS = D / 32;         // MFMA k-steps over head_dim
   constexpr int DT = D / 16;         // 16-wide head_dim tiles of the output
@@ -599,6 +673,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_direct_kernel(
   int orow[2];
   int ohead[2];
   load_q<D, G>(q, q_stride_bytes, q0, Lq, q_lo, start, g, wave, col, gq, qop, posq, orow, ohead);
+  if constexpr (FUSED)
+    store_new_rows<D, false>(const_cast<char*>(k_cache), const_cast<char*>(v_cache), k_stride_bytes, new_k, new_v,
+                             nk_stride_bytes, nv_stride_bytes, slot_mapping, q0 + q_lo, q_hi - q_lo, g, 1.f, 1.f);
 
   // Tile row r of key kt0 + r: paged rows of one block (block size >= 64, so
   // a tile never straddles blocks), or packed rows cu_k[i] + kt0 + r.
@@ -673,6 +750,36 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_direct_kernel(
                    : "memory");
     }
   };
+  // K (is_v false) or V tile at kt0 into LDS. Fused store: keys at or after
+  // `start` are this step's rows, taken from new_k / new_v (the caches are
+  // written by this launch); a tile that reaches them is loaded with one
+  // global address per lane (global_load_lds_dwordx4), rows before `start`
+  // from the caches.
+  auto issue_tile = [&](bool is_v, uint32_t lds, int kt0) {
+    const char* cache = is_v ? v_cache : k_cache;
+    const int64_t stride = is_v ? v_stride_bytes : k_stride_bytes;
+    if (!FUSED || kt0 + kKeys <= start) {
+      issue(cache, stride, is_v ? vload : kload, lds, kt0);
+      return;
+    }
+    const char* nb = is_v ? new_v : new_k;
+    const int64_t ns = is_v ? nv_stride_bytes : nk_stride_bytes;
+    const int64_t crow0 = kt0 < start ? tile_row0(kt0) : 0;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int o = (wave * LOADS + j) * 1024 + lane * 16;
+      const int r = o / ROWB;
+      const int c = ((((o % ROWB) / 16) ^ chunk_swz<D>(r)) % NCH) * 16;
+      const int t = min(kt0 + r, Lk - 1);
+      const char* src = t < start ? cache + (crow0 + (t - kt0)) * stride + head_off + c
+                                  : nb + (q0 + t - start) * ns + head_off + c;
+      const uint64_t a = reinterpret_cast<uint64_t>(src);
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                   :
+                   : "v"(a), "s"(lds + j * 1024)
+                   : "memory");
+    }
+  };
 
   // Loop-invariant LDS byte offsets of the operand reads. The swizzle of row
   // r depends on r % 16 only, so rows that differ by whole 16-row steps
@@ -721,9 +828,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_direct_kernel(
   float m[2] = {-INFINITY, -INFINITY};
   float l[2] = {0.f, 0.f};
 
-  issue(k_cache, k_stride_bytes, kload, lds_k[0], 0);
-  issue(v_cache, v_stride_bytes, vload, lds_v[0], 0);
-  if (nkt > 1) issue(k_cache, k_stride_bytes, kload, lds_k[1], kKeys);
+  issue_tile(false, lds_k[0], 0);
+  issue_tile(true, lds_v[0], 0);
+  if (nkt > 1) issue_tile(false, lds_k[1], kKeys);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   f32x4_t s_cur[4][2];
@@ -792,8 +899,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_direct_kernel(
     // is done with K(j) (read for S(j) one iteration ago) and V(j - 1)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (j + 2 < nkt) issue(k_cache, k_stride_bytes, kload, lds_k[j & 1], kt0 + 2 * kKeys);
-    if (j + 1 < nkt) issue(v_cache, v_stride_bytes, vload, lds_v[(j + 1) & 1], kt0 + kKeys);
+    if (j + 2 < nkt) issue_tile(false, lds_k[j & 1], kt0 + 2 * kKeys);
+    if (j + 1 < nkt) issue_tile(true, lds_v[(j + 1) & 1], kt0 + kKeys);
 
     f32x4_t s_next[4][2];
     Vec16 pop[2][2];
@@ -907,7 +1014,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_direct_kernel(
   write_out<D>(out, o, l, orow, ohead, num_q_heads, gq, 1.f);
 }
 
-template <int D, int G, bool FP8>
+template <int D, int G, bool FP8, bool FUSED>
 hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
   constexpr int KB = FP8 ? 1 : 2;
   constexpr int QT = kRows / G;
@@ -922,43 +1029,50 @@ hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
   const float scale_log2 = a.scale * (FP8 ? a.k_scale : 1.f) * kLog2e;
   const bool whole_rows = a.block_tables == nullptr || log2_bs >= 6;
   if (!FP8 && whole_rows) {
-    hipLaunchKernelGGL((prefill_direct_kernel<D, G>), grid, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((prefill_direct_kernel<D, G, FUSED>), grid, dim3(kThreads), 0, stream,
                        static_cast<uint16_t*>(a.out), static_cast<const char*>(a.q), a.q_stride * 2,
                        static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache),
                        a.k_stride * KB, a.v_stride * KB, a.cu_q, a.cu_k, a.block_tables, a.max_blocks,
-                       a.num_q_heads, a.num_kv_heads, log2_bs, scale_log2, max_qt);
+                       a.num_q_heads, a.num_kv_heads, log2_bs, scale_log2, max_qt,
+                       static_cast<const char*>(a.new_k), static_cast<const char*>(a.new_v), a.new_k_stride * 2,
+                       a.new_v_stride * 2, a.slot_mapping);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((prefill_kernel<D, G, FP8>), grid, dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((prefill_kernel<D, G, FP8, FUSED>), grid, dim3(kThreads), 0, stream,
                      static_cast<uint16_t*>(a.out), static_cast<const char*>(a.q), a.q_stride * 2,
                      static_cast<const char*>(a.k_cache), static_cast<const char*>(a.v_cache),
                      a.k_stride * KB, a.v_stride * KB, a.cu_q,
                      a.cu_k, a.block_tables, a.max_blocks, a.num_q_heads, a.num_kv_heads, log2_bs,
-                     scale_log2, max_qt, a.v_scale);
+                     scale_log2, max_qt, a.v_scale, static_cast<const char*>(a.new_k),
+                     static_cast<const char*>(a.new_v), a.new_k_stride * 2, a.new_v_stride * 2, a.slot_mapping,
+                     a.k_scale);
   return hipGetLastError();
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool FUSED>
 hipError_t dispatch_prefill_group(const PrefillArgs& a, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_prefill_typed<D, 1, FP8>(a, stream);
-    case 2: return launch_prefill_typed<D, 2, FP8>(a, stream);
-    case 4: return launch_prefill_typed<D, 4, FP8>(a, stream);
-    case 8: return launch_prefill_typed<D, 8, FP8>(a, stream);
-    case 16: return launch_prefill_typed<D, 16, FP8>(a, stream);
+    case 1: return launch_prefill_typed<D, 1, FP8, FUSED>(a, stream);
+    case 2: return launch_prefill_typed<D, 2, FP8, FUSED>(a, stream);
+    case 4: return launch_prefill_typed<D, 4, FP8, FUSED>(a, stream);
+    case 8: return launch_prefill_typed<D, 8, FP8, FUSED>(a, stream);
+    case 16: return launch_prefill_typed<D, 16, FP8, FUSED>(a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <bool FP8, bool FUSED>
+hipError_t dispatch_prefill_dim(const PrefillArgs& a, hipStream_t stream) {
+  return a.head_dim == 64 ? dispatch_prefill_group<64, FP8, FUSED>(a, stream)
+                          : dispatch_prefill_group<128, FP8, FUSED>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-  if (a.fp8) {
-    return a.head_dim == 64 ? dispatch_prefill_group<64, true>(a, stream)
-                            : dispatch_prefill_group<128, true>(a, stream);
-  }
-  return a.head_dim == 64 ? dispatch_prefill_group<64, false>(a, stream)
-                          : dispatch_prefill_group<128, false>(a, stream);
+  const bool fused = a.slot_mapping != nullptr;
+  if (a.fp8) return fused ? dispatch_prefill_dim<true, true>(a, stream) : dispatch_prefill_dim<true, false>(a, stream);
+  return fused ? dispatch_prefill_dim<false, true>(a, stream) : dispatch_prefill_dim<false, false>(a, stream);
 }
 
 }  // namespace pa

@@ -27,7 +27,8 @@ def test_exports_every_header_symbol(lib):
     assert set(names) == {"pa_status_string", "pa_version", "pa_store_kvcache",
                           "pa_decode_workspace_size", "pa_decode", "pa_store_decode",
                           "pa_prefill_varlen", "pa_store_kvcache_fp8", "pa_decode_fp8",
-                          "pa_store_decode_fp8", "pa_prefill_varlen_fp8"}
+                          "pa_store_decode_fp8", "pa_prefill_varlen_fp8", "pa_store_prefill",
+                          "pa_store_prefill_fp8"}
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -254,3 +255,39 @@ def test_binding_fails_loudly_without_library(tmp_path):
             mod.load(str(tmp_path / "missing.so"))
     finally:
         mod._lib = saved
+
+
+# ---- fused scatter + prefill: paged mode only, new rows packed like q ----
+
+def store_prefill(lib, fp8=False, **kw):
+    a = dict(out=A, q=A, qs=512, tq=8, key=A, ks=256, value=A, vs=256, slots=A, kc=A, vc=A, cuq=A, cuk=A,
+             mq=8, mk=8, bt=A, w=4, b=1, hq=4, hkv=2, d=128, bs=16, n=32, scale=0.1, kscale=0.02,
+             vscale=0.03, dtype=BF16)
+    a.update(kw)
+    head = (a["out"], a["q"], a["qs"], a["tq"], a["key"], a["ks"], a["value"], a["vs"], a["slots"], a["kc"],
+            a["vc"], a["cuq"], a["cuk"], a["mq"], a["mk"], a["bt"], a["w"], a["b"], a["hq"], a["hkv"], a["d"],
+            a["bs"], a["n"], a["scale"])
+    if fp8:
+        return lib.pa_store_prefill_fp8(*head, a["kscale"], a["vscale"], a["dtype"], None)
+    return lib.pa_store_prefill(*head, a["dtype"], None)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_store_prefill_validation(lib, fp8):
+    assert store_prefill(lib, fp8, b=0) == OK
+    assert store_prefill(lib, fp8, tq=0) == OK
+    assert store_prefill(lib, fp8, dtype=F32) == UNSUP
+    assert store_prefill(lib, fp8, bt=None) == NULL      # the fused call is paged only
+    assert store_prefill(lib, fp8, slots=None) == NULL
+    assert store_prefill(lib, fp8, key=None) == NULL
+    assert store_prefill(lib, fp8, value=None) == NULL
+    assert store_prefill(lib, fp8, ks=100) == SHAPE       # stride shorter than a K row
+    assert store_prefill(lib, fp8, vs=260) == ALIGN       # 520-byte rows
+    assert store_prefill(lib, fp8, key=A + 2) == ALIGN
+    assert store_prefill(lib, fp8, hq=5) == SHAPE
+    assert store_prefill(lib, fp8, d=32) == UNSUP
+    assert store_prefill(lib, fp8, bs=24) == UNSUP
+    assert store_prefill(lib, fp8, scale=0.0) == SHAPE
+    if fp8:
+        assert store_prefill(lib, fp8, kscale=0.0) == SHAPE
+        assert store_prefill(lib, fp8, vscale=float("inf")) == SHAPE
