@@ -13,7 +13,8 @@ every step reads its KV cold, as a layer's KV would be in a real model step
 
 Also measured in the same run (unless --quick): the chunked varlen prefill
 workload (16384 query tokens over 24 sequences with shared cached prefixes:
-store + pa_prefill_varlen; the metric's second half), the 8B-shaped
+store + pa_prefill_varlen; the metric's second half; the same step as one
+pa_store_prefill launch is timed too), the 8B-shaped
 large-batch decode at block sizes 16 and 256, the 131072-token
 long-context split-K decode, and the headline decode, the long-context
 decode and the chunked prefill again over fp8 (E4M3) caches.
@@ -209,9 +210,19 @@ def run_prefill(torch, binding, wl, w, steps, warmup, flush, scratch):
             binding.pa_prefill_varlen(t["q"], t["k_cache"], t["v_cache"], cuq, cuk, w.max_seqlen_q,
                                       w.max_seqlen_k, tables, w.scale, out=out)
 
+    def fused():
+        if fp8:
+            binding.pa_store_prefill_fp8(t["q"], t["k"], t["v"], slots, t["k_cache"], t["v_cache"], cuq, cuk,
+                                         w.max_seqlen_q, w.max_seqlen_k, tables, w.scale, w.k_scale,
+                                         w.v_scale, out=out)
+        else:
+            binding.pa_store_prefill(t["q"], t["k"], t["v"], slots, t["k_cache"], t["v_cache"], cuq, cuk,
+                                     w.max_seqlen_q, w.max_seqlen_k, tables, w.scale, out=out)
+
     for _ in range(warmup):
         store()
         pre()
+        fused()
     torch.cuda.synchronize()
     timer = Timer(torch, steps, 3)
     for s in range(steps):
@@ -226,6 +237,17 @@ def run_prefill(torch, binding, wl, w, steps, warmup, flush, scratch):
     assert bool(torch.isfinite(out.float()).all()), "prefill: non-finite output"
     pre_ms = sum(timer.span(1, 2)) / steps
     store_ms = sum(timer.span(0, 1)) / steps
+    step_ms = sum(timer.span(0, 2)) / steps
+    # the same step as one launch (pa_store_prefill)
+    ftimer = Timer(torch, steps, 2)
+    for s in range(steps):
+        if flush:
+            flush_caches(scratch)
+        ftimer.rec(s, 0)
+        fused()
+        ftimer.rec(s, 1)
+    torch.cuda.synchronize()
+    fused_ms = sum(ftimer.span(0, 1)) / steps
     flops = w.flops()
     res = dict(
         workload=w.name,
@@ -234,6 +256,8 @@ def run_prefill(torch, binding, wl, w, steps, warmup, flush, scratch):
         prefill_TFLOPs=flops / (pre_ms * 1e-3) / 1e12,
         store_us=1000 * store_ms,
         store_GBps=w.store_bytes() / (store_ms * 1e-3) / 1e9,
+        step_ms=step_ms,
+        fused_step_ms=fused_ms,
     )
     res["mfma_frac"] = res["prefill_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
     del t
@@ -400,12 +424,14 @@ def main():
         p = run_prefill(torch, binding, wl, wl.chunked_prefill(0), ks, 2, flush, scratch)
         torch.cuda.empty_cache()
         secondary["chunked-prefill"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in p.items()}
-        log(f"[bench] prefill {p['prefill_ms']:.3f} ms, {p['prefill_TFLOPs']:.1f} TFLOP/s")
+        log(f"[bench] prefill {p['prefill_ms']:.3f} ms, {p['prefill_TFLOPs']:.1f} TFLOP/s; "
+            f"store+prefill {p['step_ms']:.3f} ms, fused {p['fused_step_ms']:.3f} ms")
         log("[bench] chunked-prefill-fp8")
         p = run_prefill(torch, binding, wl, wl.PREFILL_CONFIGS["chunked-prefill-fp8"](0), ks, 2, flush, scratch)
         torch.cuda.empty_cache()
         secondary["chunked-prefill-fp8"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in p.items()}
-        log(f"[bench] prefill fp8 {p['prefill_ms']:.3f} ms, {p['prefill_TFLOPs']:.1f} TFLOP/s")
+        log(f"[bench] prefill fp8 {p['prefill_ms']:.3f} ms, {p['prefill_TFLOPs']:.1f} TFLOP/s; "
+            f"store+prefill {p['step_ms']:.3f} ms, fused {p['fused_step_ms']:.3f} ms")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -261,7 +261,8 @@ pa_status pa_prefill_varlen(void* out, const void* q, int64_t q_row_stride, int3
  * nothing; its row is still attended to from key / value.
  *
  *   key, value    [total_q, num_kv_heads, head_dim] bf16; row r at
- *                 key + r * key_row_stride (elements, rows 16-byte aligned).
+ *                 key + r * key_row_stride (elements, rows 16-byte aligned,
+ *                 stride at most 2^24 - 1 elements: PA_ERR_SHAPE otherwise).
  *   slot_mapping  int32 [total_q], device.
  *   k_cache, v_cache  [num_blocks, block_size, num_kv_heads, head_dim];
  *                 written at the slots, otherwise read only.
@@ -350,9 +351,11 @@ pa_status pa_prefill_varlen_fp8(void* out, const void* q, int64_t q_row_stride, 
                                 void* stream);
 
 /* pa_store_prefill over fp8 caches: bit for bit pa_store_kvcache_fp8 then
- * pa_prefill_varlen_fp8 with the same arguments (same preconditions as
- * pa_store_prefill); this step's keys and values enter the attention as their
- * E4M3 codes, exactly as the caches hold them. */
+ * pa_prefill_varlen_fp8 with the same arguments (same arguments and
+ * preconditions as pa_store_prefill, plus the scales). This one runs as those
+ * two kernels back to back on the stream: reading a new row in every query
+ * tile that needs it would quantise it once per tile, which costs more than
+ * the scatter's own launch. */
 pa_status pa_store_prefill_fp8(void* out, const void* q, int64_t q_row_stride, int32_t total_q,
                                const void* key, int64_t key_row_stride, const void* value,
                                int64_t value_row_stride, const int32_t* slot_mapping,

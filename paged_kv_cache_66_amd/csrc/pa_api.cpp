@@ -237,6 +237,8 @@ pa_status prefill_common(void* out, const void* q, int64_t q_row_stride, int32_t
     if (new_k == nullptr || new_v == nullptr) return PA_ERR_NULL;
     if ((st = check_rows(new_k, new_k_stride, row, eb)) != PA_OK) return st;
     if ((st = check_rows(new_v, new_v_stride, row, eb)) != PA_OK) return st;
+    // a tile of 64 new rows is addressed with 32-bit offsets, as packed k / v
+    if (new_k_stride > (INT32_MAX / 2) / 64 || new_v_stride > (INT32_MAX / 2) / 64) return PA_ERR_SHAPE;
   }
   pa::PrefillArgs a{};
   a.out = out;

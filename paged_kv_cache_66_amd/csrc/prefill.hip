@@ -329,17 +329,17 @@ template <> struct TileVec<true> {
 };
 
 
-// Fused store: the query rows of this workgroup are this step's new tokens.
-// Their K and V rows of kv head g (8-element chunks, packed rows of new_k /
-// new_v) go to the cache slots slot_mapping[row] (E4M3 caches: quantised with
-// k_scale / v_scale, as pa_store_kvcache_fp8 does); slot -1 stores nothing.
-// Every (row, kv head) pair belongs to exactly one workgroup.
-template <int D, bool FP8>
+// Fused store (bf16 caches): the query rows of this workgroup are this
+// step's new tokens. Their K and V rows of kv head g (16-byte chunks of the
+// packed rows of new_k / new_v) go to the cache slots slot_mapping[row]; slot
+// -1 stores nothing. Every (row, kv head) pair belongs to exactly one
+// workgroup.
+template <int D>
 __device__ __forceinline__ void store_new_rows(char* __restrict__ k_cache, char* __restrict__ v_cache,
                                                int64_t cache_row_bytes, const char* __restrict__ new_k,
                                                const char* __restrict__ new_v, int64_t nk_stride_bytes,
                                                int64_t nv_stride_bytes, const int32_t* __restrict__ slot_mapping,
-                                               int row0, int nrows, int g, float k_scale, float v_scale) {
+                                               int row0, int nrows, int g) {
   constexpr int CH = D / 8;  // 8-element chunks per head slice
   const int n = nrows * 2 * CH;
   for (int idx = threadIdx.x; idx < n; idx += blockDim.x) {
@@ -351,13 +351,9 @@ __device__ __forceinline__ void store_new_rows(char* __restrict__ k_cache, char*
     if (slot < 0) continue;
     const Vec16 x = load16((is_v ? new_v + r * nv_stride_bytes : new_k + r * nk_stride_bytes) +
                            (static_cast<int64_t>(g) * D + c * 8) * 2);
-    char* dst = (is_v ? v_cache : k_cache) + static_cast<int64_t>(slot) * cache_row_bytes +
-                (static_cast<int64_t>(g) * D + c * 8) * (FP8 ? 1 : 2);
-    if constexpr (FP8) {
-      store8(dst, quantize8(x, is_v ? v_scale : k_scale));
-    } else {
-      store16(dst, x);
-    }
+    store16((is_v ? v_cache : k_cache) + static_cast<int64_t>(slot) * cache_row_bytes +
+                (static_cast<int64_t>(g) * D + c * 8) * 2,
+            x);
   }
 }
 
@@ -369,7 +365,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
     const int32_t* __restrict__ block_tables, int32_t max_blocks, int32_t num_q_heads,
     int32_t num_kv_heads, int32_t log2_bs, float scale_log2, int32_t max_qt, float v_scale,
     const char* __restrict__ new_k, const char* __restrict__ new_v, int64_t nk_stride_bytes,
-    int64_t nv_stride_bytes, const int32_t* __restrict__ slot_mapping, float k_scale) {
+    int64_t nv_stride_bytes, const int32_t* __restrict__ slot_mapping) {
+  static_assert(!(FUSED && FP8), "E4M3 caches take the scatter as a launch of its own");
   using TV = TileVec<FP8>;
   using KVec = typename TV::Vec;
   constexpr int KB = FP8 ? 1 : 2;  // bytes per cache element
@@ -413,10 +410,6 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   int orow[2];   // packed query row, -1 when this column is padding
   int ohead[2];
   load_q<D, G>(q, q_stride_bytes, q0, Lq, q_lo, start, g, wave, col, gq, qop, posq, orow, ohead);
-  if constexpr (FUSED)
-    store_new_rows<D, FP8>(const_cast<char*>(k_cache), const_cast<char*>(v_cache), k_stride_bytes, new_k, new_v,
-                           nk_stride_bytes, nv_stride_bytes, slot_mapping, q0 + q_lo, q_hi - q_lo, g, k_scale,
-                           v_scale);
 
   // Key rows come either from the paged caches (row stride H_kv * D) through
   // the block table, or, without a table, from packed k / v tensors where key
@@ -457,7 +450,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   auto fetch = [&](int kt0) {
     if constexpr (FUSED) {
       // keys at or after `start` are this step's rows: read them from new_k
-      // / new_v (E4M3: quantised as the store does), never from the caches
+      // / new_v, never from the caches
       if (kt0 + kKeys > start) {
 #pragma unroll
         for (int u = 0; u < KLOADS; ++u) {
@@ -474,15 +467,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
           } else {
             const int64_t r = q0 + key - start;
             const int64_t ho = (static_cast<int64_t>(g) * D + c * 8) * 2;
-            const Vec16 kx = load16(new_k + r * nk_stride_bytes + ho);
-            const Vec16 vx = load16(new_v + r * nv_stride_bytes + ho);
-            if constexpr (FP8) {
-              kreg[u] = quantize8(kx, k_scale);
-              vreg[u] = quantize8(vx, v_scale);
-            } else {
-              kreg[u] = kx;
-              vreg[u] = vx;
-            }
+            kreg[u] = load16(new_k + r * nk_stride_bytes + ho);
+            vreg[u] = load16(new_v + r * nv_stride_bytes + ho);
           }
         }
         return;
@@ -600,6 +586,11 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   }
 
   write_out<D>(out, o, l, orow, ohead, num_q_heads, gq, FP8 ? v_scale : 1.f);
+  // the caches' copy of this workgroup's rows is read by no workgroup of
+  // this launch, so the scatter goes last, behind the attention
+  if constexpr (FUSED)
+    store_new_rows<D>(const_cast<char*>(k_cache), const_cast<char*>(v_cache), k_stride_bytes, new_k, new_v,
+                      nk_stride_bytes, nv_stride_bytes, slot_mapping, q0 + q_lo, q_hi - q_lo, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -673,9 +664,6 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_direct_kernel(
   int orow[2];
   int ohead[2];
   load_q<D, G>(q, q_stride_bytes, q0, Lq, q_lo, start, g, wave, col, gq, qop, posq, orow, ohead);
-  if constexpr (FUSED)
-    store_new_rows<D, false>(const_cast<char*>(k_cache), const_cast<char*>(v_cache), k_stride_bytes, new_k, new_v,
-                             nk_stride_bytes, nv_stride_bytes, slot_mapping, q0 + q_lo, q_hi - q_lo, g, 1.f, 1.f);
 
   // Tile row r of key kt0 + r: paged rows of one block (block size >= 64, so
   // a tile never straddles blocks), or packed rows cu_k[i] + kt0 + r.
@@ -751,27 +739,48 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_direct_kernel(
     }
   };
   // K (is_v false) or V tile at kt0 into LDS. Fused store: keys at or after
-  // `start` are this step's rows, taken from new_k / new_v (the caches are
-  // written by this launch); a tile that reaches them is loaded with one
-  // global address per lane (global_load_lds_dwordx4), rows before `start`
-  // from the caches.
+  // `start` are this step's rows, read from new_k / new_v (the caches' copy
+  // is written by this launch). A tile wholly past `start` is one buffer load
+  // per lane as from the caches, with the new rows' stride; the one tile that
+  // holds `start` mixes sources and takes one global address per lane
+  // (global_load_lds_dwordx4), cache rows before `start`, new rows after.
   auto issue_tile = [&](bool is_v, uint32_t lds, int kt0) {
     const char* cache = is_v ? v_cache : k_cache;
     const int64_t stride = is_v ? v_stride_bytes : k_stride_bytes;
+    const uint32_t(&off)[LOADS] = is_v ? vload : kload;
     if (!FUSED || kt0 + kKeys <= start) {
-      issue(cache, stride, is_v ? vload : kload, lds, kt0);
+      issue(cache, stride, off, lds, kt0);
       return;
     }
     const char* nb = is_v ? new_v : new_k;
     const int64_t ns = is_v ? nv_stride_bytes : nk_stride_bytes;
-    const int64_t crow0 = kt0 < start ? tile_row0(kt0) : 0;
+    const int rmax = Lk - 1 - kt0;  // rows past the keys repeat the last key
+    if (kt0 >= start) {
+      const uint64_t tile = reinterpret_cast<uint64_t>(nb + (q0 + kt0 - start) * ns + head_off);
+      u32x4_t rs;
+      rs.x = static_cast<uint32_t>(tile);
+      rs.y = static_cast<uint32_t>(tile >> 32) & 0xffffu;
+      rs.z = 0x7fffffffu;
+      rs.w = static_cast<uint32_t>(kBufferFlags);
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j) {
+        // off[j] = lrow[j] * stride + chunk: swap the row part
+        const uint32_t o = off[j] - static_cast<uint32_t>(lrow[j] * stride) +
+                           static_cast<uint32_t>(min(lrow[j], rmax) * ns);
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :
+                     : "v"(o), "s"(rs), "s"(lds + j * 1024)
+                     : "memory");
+      }
+      return;
+    }
+    const int64_t crow0 = tile_row0(kt0);
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
-      const int o = (wave * LOADS + j) * 1024 + lane * 16;
-      const int r = o / ROWB;
-      const int c = ((((o % ROWB) / 16) ^ chunk_swz<D>(r)) % NCH) * 16;
-      const int t = min(kt0 + r, Lk - 1);
-      const char* src = t < start ? cache + (crow0 + (t - kt0)) * stride + head_off + c
+      const int r = min(lrow[j], rmax);
+      const uint32_t c = off[j] - static_cast<uint32_t>(lrow[j] * stride);
+      const int t = kt0 + r;
+      const char* src = t < start ? cache + (crow0 + r) * stride + head_off + c
                                   : nb + (q0 + t - start) * ns + head_off + c;
       const uint64_t a = reinterpret_cast<uint64_t>(src);
       asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
@@ -1012,6 +1021,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_direct_kernel(
   }
 
   write_out<D>(out, o, l, orow, ohead, num_q_heads, gq, 1.f);
+  if constexpr (FUSED)  // last, as in prefill_kernel
+    store_new_rows<D>(const_cast<char*>(k_cache), const_cast<char*>(v_cache), k_stride_bytes, new_k, new_v,
+                      nk_stride_bytes, nv_stride_bytes, slot_mapping, q0 + q_lo, q_hi - q_lo, g);
 }
 
 template <int D, int G, bool FP8, bool FUSED>
@@ -1044,8 +1056,7 @@ hipError_t launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
                      a.k_stride * KB, a.v_stride * KB, a.cu_q,
                      a.cu_k, a.block_tables, a.max_blocks, a.num_q_heads, a.num_kv_heads, log2_bs,
                      scale_log2, max_qt, a.v_scale, static_cast<const char*>(a.new_k),
-                     static_cast<const char*>(a.new_v), a.new_k_stride * 2, a.new_v_stride * 2, a.slot_mapping,
-                     a.k_scale);
+                     static_cast<const char*>(a.new_v), a.new_k_stride * 2, a.new_v_stride * 2, a.slot_mapping);
   return hipGetLastError();
 }
 
@@ -1071,7 +1082,21 @@ hipError_t dispatch_prefill_dim(const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const bool fused = a.slot_mapping != nullptr;
-  if (a.fp8) return fused ? dispatch_prefill_dim<true, true>(a, stream) : dispatch_prefill_dim<true, false>(a, stream);
+  if (a.fp8) {
+    if (fused) {
+      // E4M3: every query tile that reads a new row would quantise it again
+      // (per element an fp32 division and a rounding), which costs more than
+      // the scatter's own launch; so the scatter runs first, as its own
+      // kernel, and the attention reads all keys from the caches.
+      const int32_t row_bytes = a.num_kv_heads * a.head_dim * 2;
+      const StoreArgs st{a.new_k, a.new_k_stride * 2, a.new_v, a.new_v_stride * 2,
+                         const_cast<void*>(a.k_cache), const_cast<void*>(a.v_cache), a.slot_mapping,
+                         a.total_q, row_bytes, true, a.k_scale, a.v_scale};
+      const hipError_t e = launch_store(st, stream);
+      if (e != hipSuccess) return e;
+    }
+    return dispatch_prefill_dim<true, false>(a, stream);
+  }
   return fused ? dispatch_prefill_dim<false, true>(a, stream) : dispatch_prefill_dim<false, false>(a, stream);
 }
 

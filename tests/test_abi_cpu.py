@@ -284,6 +284,7 @@ def test_store_prefill_validation(lib, fp8):
     assert store_prefill(lib, fp8, ks=100) == SHAPE       # stride shorter than a K row
     assert store_prefill(lib, fp8, vs=260) == ALIGN       # 520-byte rows
     assert store_prefill(lib, fp8, key=A + 2) == ALIGN
+    assert store_prefill(lib, fp8, ks=1 << 24) == SHAPE     # 64-row tiles use 32-bit offsets
     assert store_prefill(lib, fp8, hq=5) == SHAPE
     assert store_prefill(lib, fp8, d=32) == UNSUP
     assert store_prefill(lib, fp8, bs=24) == UNSUP
