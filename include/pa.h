@@ -355,7 +355,9 @@ pa_status pa_prefill_varlen_fp8(void* out, const void* q, int64_t q_row_stride, 
  * preconditions as pa_store_prefill, plus the scales). This one runs as those
  * two kernels back to back on the stream: reading a new row in every query
  * tile that needs it would quantise it once per tile, which costs more than
- * the scatter's own launch. */
+ * the scatter's own launch. Unlike pa_store_prefill, the attention reads
+ * this step's rows back from the caches, so a row whose slot is -1 is not
+ * seen from key / value. */
 pa_status pa_store_prefill_fp8(void* out, const void* q, int64_t q_row_stride, int32_t total_q,
                                const void* key, int64_t key_row_stride, const void* value,
                                int64_t value_row_stride, const int32_t* slot_mapping,

@@ -215,3 +215,12 @@ def test_prefill_paged_and_packed_bitwise_equal():
                                        w.max_seqlen_q, w.max_seqlen_k, None, w.scale)
     torch.cuda.synchronize()
     assert torch.equal(paged.view(torch.int16), packed.view(torch.int16))
+
+
+@pytest.mark.parametrize("bs", [16, 64])
+def test_prefill_zero_length_chunks(bs):
+    # sequences that compute no token this step sit between ones that do:
+    # their query tiles are empty and nothing is written for them
+    w = wl.custom_prefill([10, 64, 300, 0, 7], [0, 70, 0, 5, 0], block_size=bs, num_q_heads=16,
+                          num_kv_heads=4, head_dim=128, dtype="bf16", seed=bs + 31)
+    run_small(w)

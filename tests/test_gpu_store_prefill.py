@@ -147,3 +147,48 @@ def test_store_prefill_full_size(name):
     t = wl.make_device_tensors(w)
     out = _fused_vs_separate(w, t, fp8=name.endswith("fp8"))
     assert bool(torch.isfinite(out.float()).all())
+
+
+@pytest.mark.parametrize("bs", [16, 64])
+def test_store_prefill_zero_length_chunks(bs):
+    w = wl.custom_prefill([10, 64, 300, 0, 7], [0, 70, 0, 5, 0], block_size=bs, num_q_heads=16,
+                          num_kv_heads=4, head_dim=128, dtype="bf16", seed=bs + 37)
+    run_small(w)
+    run_small(wl.with_fp8_cache(w, 0.02, 0.0125), fp8=True)
+
+
+@pytest.mark.parametrize("bs", [16, 64])
+def test_store_prefill_minus_one_slots(bs):
+    """Rows whose slot is -1 are not stored, yet the attention still sees
+    them (it reads this step's keys from key / value): the output equals the
+    oracle over caches holding every row, and those slots keep their old
+    contents."""
+    import torch
+    w = wl.custom_prefill([0, 100, 64], [90, 70, 5], block_size=bs, num_q_heads=16, num_kv_heads=4,
+                          head_dim=128, dtype="bf16", seed=bs + 41)
+    t = wl.make_host_tensors(w)
+    drop = np.zeros(w.total_q, dtype=bool)
+    drop[[0, 1, 45, 89, 90, 130, 159, w.total_q - 1]] = True
+    slots = np.where(drop, -1, w.slot_mapping).astype(np.int32)
+    hq, hkv, d, tq = w.num_q_heads, w.num_kv_heads, w.head_dim, w.total_q
+    qkv = to_device(t["qkv"], "bf16")
+    q = qkv[:, : hq * d].view(tq, hq, d)
+    k = qkv[:, hq * d:(hq + hkv) * d].view(tq, hkv, d)
+    v = qkv[:, (hq + hkv) * d:].view(tq, hkv, d)
+    kc, vc = to_device(t["k_cache"], "bf16"), to_device(t["v_cache"], "bf16")
+    print(f"[store-prefill -1 slots] bs={bs} dropped={int(drop.sum())}", flush=True)
+    out = binding.pa_store_prefill(q, k, v, torch.from_numpy(slots).cuda(), kc, vc,
+                                   torch.from_numpy(w.cu_seqlens_q).cuda(), torch.from_numpy(w.cu_seqlens_k).cuda(),
+                                   w.max_seqlen_q, w.max_seqlen_k, torch.from_numpy(w.block_tables).cuda(), w.scale)
+    torch.cuda.synchronize()
+    kc_all, vc_all = t["k_cache"].copy(), t["v_cache"].copy()
+    oracle.store_kvcache(t["k"], t["v"], kc_all, vc_all, w.slot_mapping)
+    ref = oracle.prefill_varlen(t["q"], kc_all, vc_all, w.cu_seqlens_q, w.cu_seqlens_k, w.block_tables,
+                                w.scale, "bf16")
+    assert_attention_close(widen_host(to_host(out, "bf16"), "bf16"), ref, "bf16", "-1 slots")
+    kc_want, vc_want = t["k_cache"].copy(), t["v_cache"].copy()
+    oracle.store_kvcache(t["k"], t["v"], kc_want, vc_want, slots)
+    got_k, got_v = to_host(kc, "bf16"), to_host(vc, "bf16")
+    # NaN-poisoned slots compare by bit pattern
+    assert np.array_equal(got_k.view(np.uint16), kc_want.view(np.uint16))
+    assert np.array_equal(got_v.view(np.uint16), vc_want.view(np.uint16))
