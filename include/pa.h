@@ -13,6 +13,9 @@
  *                      values (cached prefix + this step's chunk) are read
  *                      through the block tables.
  *
+ * pa_store_decode and pa_store_prefill do a step's scatter and its attention
+ * in one call; the *_fp8 entry points keep E4M3 caches.
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * Ownership.  Every pointer argument is a device pointer owned by the caller
