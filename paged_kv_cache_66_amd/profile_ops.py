@@ -9,6 +9,8 @@ Operations:
   store_decode <workload>  the same step as one pa_store_decode launch;
   prefill [workload]  pa_store_kvcache + pa_prefill_varlen on chunked-prefill
                       (or chunked-prefill-fp8: the _fp8 entry points);
+  store_prefill [workload]  the same step as one pa_store_prefill call
+                      (pa_store_prefill_fp8 over fp8 caches);
   copy                a 1 GiB device-to-device copy (counter calibration:
                       reads 1 GiB, writes 1 GiB).
 Workloads are the seeded synthetic ones of ``workloads.py``; a workload over
@@ -27,7 +29,7 @@ if ROOT not in sys.path:
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("op", choices=["decode", "store_decode", "prefill", "copy"])
+    ap.add_argument("op", choices=["decode", "store_decode", "prefill", "store_prefill", "copy"])
     ap.add_argument("workload", nargs="?", default="qwen3-0.6b-decode")
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--partition", type=int, default=0)
@@ -44,7 +46,7 @@ def main(argv=None):
         dst = torch.empty_like(scratch)
         for _ in range(args.reps):
             dst.copy_(scratch)
-    elif args.op == "prefill":
+    elif args.op in ("prefill", "store_prefill"):
         name = args.workload if args.workload in wl.PREFILL_CONFIGS else "chunked-prefill"
         w = wl.PREFILL_CONFIGS[name](0)
         fp8 = w.cache_dtype == "fp8e4m3"
@@ -56,6 +58,12 @@ def main(argv=None):
         out = torch.empty((w.total_q, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
         for _ in range(args.reps):
             scratch.amax()
+            if args.op == "store_prefill":
+                fused = binding.pa_store_prefill_fp8 if fp8 else binding.pa_store_prefill
+                extra = (w.k_scale, w.v_scale) if fp8 else ()
+                fused(t["q"], t["k"], t["v"], slots, t["k_cache"], t["v_cache"], cuq, cuk, w.max_seqlen_q,
+                      w.max_seqlen_k, tables, w.scale, *extra, out=out)
+                continue
             if fp8:
                 binding.pa_store_kvcache_fp8(t["k"], t["v"], t["k_cache"], t["v_cache"], slots, w.k_scale,
                                              w.v_scale)
