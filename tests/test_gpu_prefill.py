@@ -224,3 +224,39 @@ def test_prefill_zero_length_chunks(bs):
     w = wl.custom_prefill([10, 64, 300, 0, 7], [0, 70, 0, 5, 0], block_size=bs, num_q_heads=16,
                           num_kv_heads=4, head_dim=128, dtype="bf16", seed=bs + 31)
     run_small(w)
+
+
+@pytest.mark.parametrize("bs,cached,sched", [(256, [4096], [8192]), (16, [1000], [3000])])
+def test_prefill_long_single_sequence_sampled(bs, cached, sched):
+    """One long sequence (hundreds of 64-key tiles per query tile, dozens of
+    query tiles): sampled rows, the first and last rows and every query tile
+    edge in a stretch, against the oracle; also the fused call, bitwise."""
+    import torch
+    w = wl.custom_prefill(cached, sched, block_size=bs, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                          dtype="bf16", seed=bs + 53)
+    print(f"[prefill-long] bs={bs} cached={cached} sched={sched}", flush=True)
+    t = wl.make_device_tensors(w)
+    kc_h, vc_h = to_host(t["k_cache"], "bf16"), to_host(t["v_cache"], "bf16")
+    q_h, k_h, v_h = (to_host(t[x], "bf16") for x in ("q", "k", "v"))
+    kc2, vc2 = t["k_cache"].clone(), t["v_cache"].clone()
+    slots = torch.from_numpy(w.slot_mapping).cuda()
+    cuq, cuk = torch.from_numpy(w.cu_seqlens_q).cuda(), torch.from_numpy(w.cu_seqlens_k).cuda()
+    tables = torch.from_numpy(w.block_tables).cuda()
+    binding.pa_store_kvcache(t["k"], t["v"], t["k_cache"], t["v_cache"], slots)
+    out = binding.pa_prefill_varlen(t["q"], t["k_cache"], t["v_cache"], cuq, cuk, w.max_seqlen_q,
+                                    w.max_seqlen_k, tables, w.scale)
+    fused = binding.pa_store_prefill(t["q"], t["k"], t["v"], slots, kc2, vc2, cuq, cuk, w.max_seqlen_q,
+                                     w.max_seqlen_k, tables, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), fused.view(torch.int16))
+    assert torch.equal(t["k_cache"].view(torch.int16), kc2.view(torch.int16))
+    oracle.store_kvcache(k_h, v_h, kc_h, vc_h, w.slot_mapping)
+    rng = np.random.default_rng(5)
+    tq = w.total_q
+    rows = sorted(set([0, 1, 31, 32, 33, tq - 1, tq - 2] + list(range(2000, 2100, 7)) +
+                      [int(x) for x in rng.integers(0, tq, 24)]))
+    ref = oracle.prefill_varlen(q_h, kc_h, vc_h, w.cu_seqlens_q, w.cu_seqlens_k, w.block_tables, w.scale,
+                                "bf16", rows=rows)
+    got = widen_host(to_host(out, "bf16"), "bf16")
+    err = assert_attention_close(got[rows], ref[rows], "bf16", "long single sequence")
+    print(f"[prefill-long] {len(rows)} rows, max err {err:.3e}", flush=True)
