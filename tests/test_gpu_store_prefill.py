@@ -192,3 +192,25 @@ def test_store_prefill_minus_one_slots(bs):
     # NaN-poisoned slots compare by bit pattern
     assert np.array_equal(got_k.view(np.uint16), kc_want.view(np.uint16))
     assert np.array_equal(got_v.view(np.uint16), vc_want.view(np.uint16))
+
+
+@pytest.mark.parametrize("bs", [16, 64])
+def test_store_prefill_distinct_key_value_strides(bs):
+    """key contiguous ([T, H_kv, D], row stride H_kv*D), value a row-strided
+    view of a wider buffer: each side uses its own stride."""
+    import torch
+    w = wl.custom_prefill([0, 100, 64], [90, 70, 5], block_size=bs, num_q_heads=16, num_kv_heads=4,
+                          head_dim=128, dtype="bf16", seed=bs + 61)
+    t = wl.make_host_tensors(w)
+    hq, hkv, d, tq = w.num_q_heads, w.num_kv_heads, w.head_dim, w.total_q
+    qkv = to_device(t["qkv"], "bf16")
+    dev = {"q": qkv[:, : hq * d].view(tq, hq, d),
+           "k": qkv[:, hq * d:(hq + hkv) * d].reshape(tq, hkv, d).contiguous(),
+           "v": qkv[:, (hq + hkv) * d:].view(tq, hkv, d),
+           "k_cache": to_device(t["k_cache"], "bf16"), "v_cache": to_device(t["v_cache"], "bf16")}
+    assert dev["k"].stride(0) != dev["v"].stride(0)
+    fused = _fused_vs_separate(w, dev, fp8=False)
+    kc, vc = t["k_cache"].copy(), t["v_cache"].copy()
+    oracle.store_kvcache(t["k"], t["v"], kc, vc, w.slot_mapping)
+    ref = oracle.prefill_varlen(t["q"], kc, vc, w.cu_seqlens_q, w.cu_seqlens_k, w.block_tables, w.scale, "bf16")
+    assert_attention_close(widen_host(to_host(fused, "bf16"), "bf16"), ref, "bf16", "distinct strides")
