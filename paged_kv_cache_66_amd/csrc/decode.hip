@@ -213,6 +213,9 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   constexpr int LPT = D / EPV;       // lanes per (token, kv head) row
   constexpr int TPW = 64 / LPT;      // rows per wave per load
   constexpr int STEP = kWaves * TPW; // rows per workgroup per load
+  // value pass: 16 loads in flight per lane, so a 256-token partition's V
+  // rows come in one trip
+  constexpr int kUnrollV = 16;
 
   // fused: the new row's K and V head slices, in cache format, come first
   constexpr int kNewWords = FUSED ? 2 * D * EB / 4 : 0;
@@ -406,10 +409,10 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 #pragma unroll
     for (int e = 0; e < EPV; ++e) acc[h][e] = 0.f;
 
-  for (int base = 0; base < nloop; base += STEP * kUnroll) {
-    Vec vv[kUnroll];
+  for (int base = 0; base < nloop; base += STEP * kUnrollV) {
+    Vec vv[kUnrollV];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kUnrollV; ++u) {
       const int tl = base + u * STEP + my_row;
       if (tl < nloop) {
         vv[u] = E::load_nt(vbase + row_off(tl));
@@ -418,7 +421,7 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
       }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kUnrollV; ++u) {
       const int tl = base + u * STEP + my_row;
       if (tl < nloop) {
         float vf[EPV];
