@@ -51,8 +51,8 @@ def log(msg):
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
