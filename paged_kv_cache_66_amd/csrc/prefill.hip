@@ -328,7 +328,6 @@ template <> struct TileVec<true> {
   }
 };
 
-
 // Fused store (bf16 caches): the query rows of this workgroup are this
 // step's new tokens. Their K and V rows of kv head g (16-byte chunks of the
 // packed rows of new_k / new_v) go to the cache slots slot_mapping[row]; slot
