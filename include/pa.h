@@ -269,7 +269,8 @@ pa_status pa_prefill_varlen(void* out, const void* q, int64_t q_row_stride, int3
  *   slot_mapping  int32 [total_q], device.
  *   k_cache, v_cache  [num_blocks, block_size, num_kv_heads, head_dim];
  *                 written at the slots, otherwise read only.
- *   block_tables  must not be NULL (PA_ERR_NULL), nor slot_mapping.
+ *   block_tables  must not be NULL (PA_ERR_NULL), nor slot_mapping unless the
+ *                 step has no query token (total_q or num_seqs 0: nothing runs).
  * Everything else as pa_prefill_varlen in paged mode, including the error
  * codes; only PA_BF16.
  */

@@ -432,7 +432,9 @@ pa_status pa_store_prefill(void* out, const void* q, int64_t q_row_stride, int32
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                            int32_t num_blocks, float scale, pa_dtype dtype, void* stream) {
   if (dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
-  if (block_tables == nullptr || slot_mapping == nullptr) return PA_ERR_NULL;
+  if (block_tables == nullptr) return PA_ERR_NULL;  // the fused call is paged only
+  // an empty step stores nothing, so its slot mapping may be absent
+  if (slot_mapping == nullptr && total_q > 0 && num_seqs > 0) return PA_ERR_NULL;
   return prefill_common(out, q, q_row_stride, total_q, k_cache, 0, v_cache, 0, cu_seqlens_q,
                         cu_seqlens_k, max_seqlen_q, max_seqlen_k, block_tables,
                         max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim,
@@ -450,7 +452,8 @@ pa_status pa_store_prefill_fp8(void* out, const void* q, int64_t q_row_stride, i
                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                int32_t num_blocks, float scale, float k_scale, float v_scale,
                                pa_dtype dtype, void* stream) {
-  if (block_tables == nullptr || slot_mapping == nullptr) return PA_ERR_NULL;
+  if (block_tables == nullptr) return PA_ERR_NULL;
+  if (slot_mapping == nullptr && total_q > 0 && num_seqs > 0) return PA_ERR_NULL;
   return prefill_common(out, q, q_row_stride, total_q, k_cache, 0, v_cache, 0, cu_seqlens_q,
                         cu_seqlens_k, max_seqlen_q, max_seqlen_k, block_tables,
                         max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim,

@@ -279,6 +279,7 @@ def test_store_prefill_validation(lib, fp8):
     assert store_prefill(lib, fp8, dtype=F32) == UNSUP
     assert store_prefill(lib, fp8, bt=None) == NULL      # the fused call is paged only
     assert store_prefill(lib, fp8, slots=None) == NULL
+    assert store_prefill(lib, fp8, slots=None, key=None, value=None, tq=0) == OK  # empty step
     assert store_prefill(lib, fp8, key=None) == NULL
     assert store_prefill(lib, fp8, value=None) == NULL
     assert store_prefill(lib, fp8, ks=100) == SHAPE       # stride shorter than a K row
