@@ -173,6 +173,7 @@ def run_decode(torch, binding, wl, w, steps, warmup, flush, scratch, partition=0
         decode_ms_p10_p90=[sorted(dec_ms)[steps // 10], sorted(dec_ms)[(9 * steps) // 10]],
         store_us=1000 * sum(store_ms) / steps,
         fused_step_ms=fused_ms,
+        fused_ms_median=sorted(fused_list)[steps // 2],
         fused_ms_p10_p90=[sorted(fused_list)[steps // 10], sorted(fused_list)[(9 * steps) // 10]],
         bytes_logical=w.algorithmic_bytes(unique=False),
         bytes_unique=w.algorithmic_bytes(unique=True),
@@ -235,7 +236,8 @@ def run_prefill(torch, binding, wl, w, steps, warmup, flush, scratch):
         timer.rec(s, 2)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(out.float()).all()), "prefill: non-finite output"
-    pre_ms = sum(timer.span(1, 2)) / steps
+    pre_list = timer.span(1, 2)
+    pre_ms = sum(pre_list) / steps
     store_ms = sum(timer.span(0, 1)) / steps
     step_ms = sum(timer.span(0, 2)) / steps
     # the same step as one launch (pa_store_prefill)
@@ -252,6 +254,8 @@ def run_prefill(torch, binding, wl, w, steps, warmup, flush, scratch):
     res = dict(
         workload=w.name,
         prefill_ms=pre_ms,
+        prefill_ms_median=sorted(pre_list)[steps // 2],
+        prefill_ms_p10_p90=[sorted(pre_list)[steps // 10], sorted(pre_list)[(9 * steps) // 10]],
         flops=flops,
         prefill_TFLOPs=flops / (pre_ms * 1e-3) / 1e12,
         store_us=1000 * store_ms,
@@ -485,6 +489,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "components": {
+            "fused_step_ms_median": round(head["fused_ms_median"], 5),
             "fused_step_ms_p10_p90": [round(x, 5) for x in head["fused_ms_p10_p90"]],
             "two_call_step_ms": round(head["step_ms"], 5),
             "decode_ms": round(head["decode_ms"], 5),
