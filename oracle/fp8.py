@@ -17,13 +17,14 @@ listed in the design notes of the repository):
 * scaling: one fp32 scale per cache tensor (k_scale for K, v_scale for V).
   A stored code c stands for value(c) * scale.
 * quantising a value x (held in the input's storage type) for the cache:
-  y = fp32(|x|) / fp32(scale), the fp32 quotient rounded to nearest; then the
-  finite E4M3 value nearest to y, ties to the code with an even mantissa;
-  magnitudes of 448 and beyond (infinities included) saturate to 448; a NaN
-  gives the NaN code. The code's sign bit is x's sign bit (so -0 and a
-  negative NaN keep it; the sign of a NaN quotient is left to no hardware).
-  The quotient is taken in fp32 because that is the precision the device
-  takes it in, and the code is an integer decided by it.
+  the finite E4M3 value nearest to the real number y = |x| / scale (scale as
+  the fp32 value the library receives), ties to the code with an even
+  mantissa; magnitudes of 448 and beyond (infinities included) saturate to
+  448; a NaN gives the NaN code. The code's sign bit is x's sign bit (so -0
+  and a negative NaN keep it; the sign of a NaN quotient is left to no
+  hardware). This is the plain reading of "store x / scale as E4M3": the
+  exact quotient is rounded once, with no intermediate rounding of the
+  quotient to some working precision.
 """
 from __future__ import annotations
 
@@ -95,15 +96,30 @@ def encode(y) -> np.ndarray:
 
 
 def quantize(x64: np.ndarray, scale: float) -> np.ndarray:
-    """Codes for exact input values ``x64`` (already widened from their
-    storage type, so exactly representable in fp32) under a per-tensor
-    scale: the magnitude code of y = fp32(|x|) / fp32(scale) taken in fp32,
-    with x's sign bit."""
-    with np.errstate(over="ignore", invalid="ignore"):  # inf / NaN inputs are part of the domain
-        x32 = np.asarray(x64, dtype=np.float64).astype(np.float32)
-        y = np.abs(x32) / np.float32(scale)
-    mag = encode(y.astype(np.float64)) & 0x7F
-    return (mag | np.where(np.signbit(x32), 0x80, 0)).astype(np.uint8)
+    """Codes for exact input values ``x64`` (widened from their storage type)
+    under a per-tensor scale: the finite E4M3 value nearest the real quotient
+    y = |x| / s with s = fp32(scale), ties to the even mantissa, 448 and
+    beyond saturating, NaN giving the NaN code, with x's sign bit.
+
+    No quotient is formed. With v_0 < v_1 < ... < v_126 = 448 the finite
+    non-negative E4M3 values, y lies between v_lo and v_hi = the first value
+    with v * s >= |x|, and the half-way point m = (v_lo + v_hi) / 2 decides:
+    |x| < m * s picks lo, |x| > m * s picks hi, equality is a tie. Every v
+    and m has at most 5 significant bits and s at most 24, so v * s and m * s
+    are exact in fp64, as is |x|: each comparison is decided exactly."""
+    s = float(np.float32(scale))
+    x = np.asarray(x64, dtype=np.float64)
+    nan = np.isnan(x)
+    a = np.where(nan, 0.0, np.abs(x))
+    thresholds = _POS_VALUES * s                                        # v_k * s, exact
+    hi = np.clip(np.searchsorted(thresholds, a, side="left"), 0, 0x7E)  # first v_k * s >= |x|
+    lo = np.maximum(hi - 1, 0)
+    mid_s = (_POS_VALUES[lo] + _POS_VALUES[hi]) / 2 * s                 # m * s, exact
+    code = np.where(a < mid_s, lo, np.where(a > mid_s, hi, np.where(lo & 1, hi, lo)))
+    code = np.where(a >= 448.0 * s, 0x7E, code)                         # y >= 448 saturates
+    code = np.where(np.isnan(x), 0x7F, code)                            # NaN keeps a NaN code
+    sign = np.where(np.signbit(x), 0x80, 0)
+    return (code | sign).astype(np.uint8)
 
 
 def dequantize(codes, scale: float) -> np.ndarray:

@@ -3,8 +3,11 @@
 * library routine: torch's float8_e4m3fn type (its own implementation of the
   OCP format) gives the value of every one of the 256 codes, and its
   float32 -> float8_e4m3fn cast (round to nearest even) gives the code of
-  every value below the saturation threshold, ties included; torch's fp32
-  division gives the quotient the quantiser must round;
+  every value below the saturation threshold, ties included, and so the
+  code of every quotient that is not itself a half-way point;
+* brute force in exact rational arithmetic (fractions.Fraction) for the
+  quantiser: the nearest value to |x| / scale over all 127 finite values,
+  on every input whose fp32 quotient is a half-way point and on a sample;
 * closed forms worked by hand from the field definition (1.0, the largest
   value, the subnormal ladder, half-way cases, saturation, NaN, signed zero);
 * invariants: every finite code survives encode(decode(c)); encoding is
@@ -119,33 +122,80 @@ def pin_round_trip_and_order(f):
     assert np.max(np.abs(v - np.clip(ys, -448, 448)) / np.maximum(np.abs(ys), 2.0 ** -6)) <= 2.0 ** -4 + 1e-12
 
 
-def pin_quantize_fp32_quotient(f):
-    """The code is decided on the fp32 quotient (torch's fp32 division then
-    torch's cast), including inputs whose fp32 quotient lands exactly on a
-    half-way point while the exact quotient does not."""
+# scales whose fp32 quotients land exactly on E4M3 half-way points for some
+# bf16 inputs while the exact quotient does not (16/19 and 1/3 give about 30
+# such inputs each over the 65536 bf16 patterns, 0.0125, 1.7, 8/11 and 0.1 two)
+TIE_SCALES = (16 / 19, 1 / 3, 0.0125, 1.7, 8 / 11, 0.1)
+
+
+def _exact_code(x: float, scale: float) -> int:
+    """Brute force from the definition, in exact rational arithmetic: the
+    finite E4M3 value (torch's table) nearest |x| / fp32(scale), ties to the
+    even code, 448 and beyond saturating, with x's sign."""
+    from fractions import Fraction
+    sign = 0x80 if np.signbit(x) else 0
+    if np.isnan(x):
+        return sign | 0x7F
+    if np.isinf(x):
+        return sign | 0x7E
+    y = Fraction(abs(float(x))) / Fraction(float(np.float32(scale)))
+    if y >= 448:
+        return sign | 0x7E
+    dist = [abs(Fraction(float(v)) - y) for v in _torch_values()[:0x7F]]
+    best = min(dist)
+    cands = [c for c in range(0x7F) if dist[c] == best]
+    return sign | (cands[0] if len(cands) == 1 else [c for c in cands if c % 2 == 0][0])
+
+
+def pin_quantize_exact_quotient(f):
+    """The code is the exact quotient's, rounded once. Over every finite bf16
+    pattern at scales that provoke the hard cases: where the fp32 quotient
+    (numpy's correctly rounded fp32 division) is not an E4M3 half-way point,
+    the exact quotient lies in the same rounding interval, so torch's
+    fp32 -> float8_e4m3fn cast of it gives the code; where it is one, the
+    Fraction brute force decides. Some of those inputs must round away from
+    the fp32 quotient's tie, or the battery would not tell the readings
+    apart. A random sample also goes through the brute force directly."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):
+        x64 = oracle.widen(bits, "bf16")
+    x64 = x64[np.isfinite(x64)]
+    vals = _torch_values()
+    fin = np.sort(np.unique(vals[np.isfinite(vals) & (vals >= 0)]))
+    mids32 = ((fin[:-1] + fin[1:]) / 2).astype(np.float32)
+    sign = np.where(np.signbit(x64), 0x80, 0)
+    away = 0
+    for scale in (1.0, 3.0, 100.0) + TIE_SCALES:
+        got = f.quantize(x64, scale)
+        with np.errstate(over="ignore"):
+            y32 = np.abs(x64.astype(np.float32)) / np.float32(scale)
+        on_mid = np.isin(y32, mids32)
+        keep = ~on_mid & (y32 < 448)
+        assert np.array_equal(got[keep], _torch_encode(y32[keep]) | sign[keep]), scale
+        assert np.all(got[~on_mid & (y32 >= 448)] & 0x7F == 0x7E), scale
+        for x, c, y in zip(x64[on_mid], got[on_mid], y32[on_mid]):
+            want = _exact_code(float(x), scale)
+            assert c == want, (float(x), scale, hex(c), hex(want))
+            away += int(want & 0x7F) != int(_torch_encode(np.array([y]))[0])
+    assert away >= 30, away
     rng = np.random.default_rng(1)
-    x = wl.f32_to_bf16_bits(rng.standard_normal(4000).astype(np.float32) * 3)
-    x64 = oracle.widen(x, "bf16")
-    for scale in (0.013, 0.3, 1.0, 1.7, 3.0):
-        y32 = (torch.from_numpy(x64.astype(np.float32)) / torch.tensor(scale, dtype=torch.float32)).numpy()
-        keep = np.abs(y32) < 448
-        assert np.array_equal(f.quantize(x64, scale)[keep], _torch_encode(y32[keep]))
-        assert np.all(f.quantize(x64, scale)[~keep] & 0x7F == 0x7E)
-    # scales just above 1 and inputs x = fp32(1.0625 * scale) whose exact
-    # quotient lies above the half-way point 1.0625 while the fp32 quotient is
-    # exactly on it: the fp32 tie goes to the even mantissa (1.0, code 0x38),
-    # where the exact quotient would round up to 1.125 (0x39)
+    xs = oracle.widen(wl.f32_to_bf16_bits(rng.standard_normal(600).astype(np.float32) * 4), "bf16")
+    for scale in (0.013, 0.7, 16 / 19):
+        got = f.quantize(xs, scale)
+        assert [int(c) for c in got] == [_exact_code(float(x), scale) for x in xs], scale
+    # fp32 inputs x = fp32(1.0625 * scale), scale just above 1: the fp32
+    # quotient is exactly the half-way point 1.0625 while the exact quotient
+    # lies above it, so the code is 1.125 (0x39), not the tie's even 1.0
     mid = 1.0625
     cases = []
     for k in range(1, 20000):
         scale = np.float32(1.0 + k * 2.0 ** -23)
         x32 = np.float32(mid * float(scale))
-        q32 = (torch.tensor(float(x32), dtype=torch.float32) / torch.tensor(float(scale), dtype=torch.float32)).item()
-        if q32 == mid and float(x32) / float(scale) > mid:
+        if np.float32(x32 / scale) == mid and float(x32) / float(scale) > mid:
             cases.append((float(x32), float(scale)))
     assert cases, "no fp32-tie case found"
     for x, scale in cases[:20]:
-        assert f.quantize(np.array([x]), scale)[0] == 0x38, (x, scale)
+        assert f.quantize(np.array([x]), scale)[0] == 0x39 == _exact_code(x, scale), (x, scale)
 
 
 def pin_quantize_specials(f):
@@ -209,7 +259,7 @@ def pin_attention_with_fp8_cache(f):
 
 
 PINS = [pin_value_table, pin_encode_vs_torch, pin_vector_encode_matches_scalar, pin_closed_forms, pin_round_trip_and_order,
-        pin_quantize_fp32_quotient, pin_quantize_specials, pin_store_rows, pin_attention_with_fp8_cache]
+        pin_quantize_exact_quotient, pin_quantize_specials, pin_store_rows, pin_attention_with_fp8_cache]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -236,11 +286,19 @@ MUTANTS = [
     ("vector always rounds down", "code = np.where(d_lo < d_hi, lo,", "code = np.where(d_lo <= d_hi + 1e9, lo,"),
     ("vector bracket off by one", "lo = np.clip(hi - 1, 0, 0x7E)", "lo = np.clip(hi - 2, 0, 0x7E)"),
     ("vector NaN is zero", "code = np.where(nan, 0x7F, code)", "code = code"),
-    ("fp64 quotient", "        y = np.abs(x32) / np.float32(scale)",
-     "        y = np.abs(np.asarray(x64, dtype=np.float64)) / float(np.float32(scale))"),
-    ("scale multiplies on store", "        y = np.abs(x32) / np.float32(scale)", "        y = np.abs(x32) * np.float32(scale)"),
-    ("store drops the sign", "return (mag | np.where(np.signbit(x32), 0x80, 0)).astype(np.uint8)",
-     "return mag.astype(np.uint8)"),
+    ("fp32 quotient rounded twice",
+     "    code = np.where(a < mid_s, lo, np.where(a > mid_s, hi, np.where(lo & 1, hi, lo)))",
+     "    code = encode((a.astype(np.float32) / np.float32(s)).astype(np.float64)) & 0x7F"),
+    ("quantiser ties away from zero", "np.where(lo & 1, hi, lo)", "hi"),
+    ("quantiser ties to odd", "np.where(lo & 1, hi, lo)", "np.where(lo & 1, lo, hi)"),
+    ("quantiser NaN saturates", "code = np.where(np.isnan(x), 0x7F, code)", "code = np.where(np.isnan(x), 0x7E, code)"),
+    ("quantiser bracket off by one", "lo = np.maximum(hi - 1, 0)", "lo = np.maximum(hi - 2, 0)"),
+    ("half-way point not scaled", "mid_s = (_POS_VALUES[lo] + _POS_VALUES[hi]) / 2 * s",
+     "mid_s = (_POS_VALUES[lo] + _POS_VALUES[hi]) / 2"),
+    ("saturation threshold not scaled", "code = np.where(a >= 448.0 * s, 0x7E, code)",
+     "code = np.where(a >= 448.0, 0x7E, code)"),
+    ("scale multiplies on store", "    s = float(np.float32(scale))\n", "    s = 1.0 / float(np.float32(scale))\n"),
+    ("store drops the sign", "return (code | sign).astype(np.uint8)", "return code.astype(np.uint8)"),
     ("dequantize ignores scale", "return decode(codes) * float(np.float32(scale))", "return decode(codes)"),
     ("store skips slot 0", "if s < 0:", "if s <= 0:"),
     ("V stored with the K scale", "v_cache[block, offset] = quantize(value64[t], v_scale)",
