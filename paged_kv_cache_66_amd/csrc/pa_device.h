@@ -98,12 +98,38 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Cache code of x under a per-tensor scale: the E4M3 code of |x| / scale
-// (fp32 division, correctly rounded) carrying x's sign bit, so -0 and NaN
-// keep their sign whatever sign the hardware gives a NaN quotient.
+// Whether a non-negative fp32 value (bits u) is exactly a rounding midpoint
+// between two neighbouring E4M3 values: in the normal range (2^-6 .. 448)
+// the 20 mantissa bits below the kept 3 read 1000..0; below 2^-6 the value
+// is an odd multiple of 2^-10 (so u * 512 has fraction one half; the
+// product and the fraction are exact).
+__host__ __device__ __forceinline__ bool e4m3_midpoint(uint32_t u) {
+  if (u >= 0x3c800000u) return u < 0x43e00000u && (u & 0xfffffu) == 0x80000u;
+  const float t = __builtin_bit_cast(float, u) * 512.f;
+  return t - __builtin_floorf(t) == 0.5f;
+}
+
+// Cache code of x under a per-tensor scale: the E4M3 code nearest the exact
+// quotient |x| / scale, carrying x's sign bit (so -0 and NaN keep their
+// sign whatever sign the hardware gives a NaN quotient).
+// The correctly rounded fp32 quotient q lies in the same E4M3 rounding
+// interval as the exact quotient unless q is itself a midpoint; there the
+// exact quotient may be on either side. Its side is the sign of the remainder
+// |x| - q * scale, which fp64 gives exactly (q * scale has at most 48
+// significant bits, and the two terms are within a factor of two of each
+// other), and q is moved one fp32 ulp that way before it is rounded, so a
+// true tie (remainder 0) still goes to the even code.
 __host__ __device__ __forceinline__ uint32_t e4m3_quantize(float x, float scale) {
   const uint32_t sign = (__builtin_bit_cast(uint32_t, x) >> 24) & 0x80u;
-  return sign | (f32_to_e4m3(fabsf(x) / scale) & 0x7fu);
+  const float a = fabsf(x);
+  const float q = a / scale;
+  uint32_t qb = __builtin_bit_cast(uint32_t, q);
+  if (e4m3_midpoint(qb)) {
+    const double r = static_cast<double>(a) - static_cast<double>(q) * static_cast<double>(scale);
+    qb += (r > 0.0) ? 1u : 0u;
+    qb -= (r < 0.0) ? 1u : 0u;
+  }
+  return sign | (f32_to_e4m3(__builtin_bit_cast(float, qb)) & 0x7fu);
 }
 
 // E4M3 codes of eight consecutive elements of a bf16 row under a scale.

@@ -9,8 +9,10 @@
   made visible through a one-hot query;
 * decode and prefill over fp8 caches element by element on small varlen
   workloads (every group size, both head dims, block sizes, split and single
-  pass), fused store+decode bit-identical to store then decode, and sampled
-  rows of the full-size workloads in the benchmark's launch configuration.
+  pass), fused store+decode bit-identical to store then decode, and the
+  full-size workloads in the benchmark's launch configuration (every decode
+  sequence; every row of one prefill sequence and one row of every query
+  tile), into NaN-filled outputs.
 """
 import numpy as np
 import pytest
@@ -18,6 +20,7 @@ import pytest
 import oracle
 from paged_kv_cache_66_amd import binding
 from paged_kv_cache_66_amd import workloads as wl
+from tests import fullsize
 from tests.helpers import assert_attention_close, gpu_available, to_device, to_host, widen_host
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -43,8 +46,12 @@ def _torch_code_values_bf16(codes: np.ndarray) -> np.ndarray:
 # store
 # ---------------------------------------------------------------------------
 
+# (16/19, 1/3), (8/11, 0.1) and (1.7, 0.0125) put the fp32 quotient of some
+# bf16 inputs exactly on an E4M3 half-way point while the exact quotient is
+# off it: the code must follow the exact quotient
 @pytest.mark.parametrize("k_scale,v_scale", [(1.0, 1.0), (0.0125, 0.02), (100.0, 3.0), (2.0 ** -6, 0.3),
-                                             (7.3e-3, 1e-3)])
+                                             (7.3e-3, 1e-3), (16 / 19, 1 / 3), (8 / 11, 0.1),
+                                             (1.7, 0.0125)])
 def test_store_fp8_every_bf16_pattern(k_scale, v_scale):
     import torch
     hkv, d, bs = 2, 128, 16
@@ -201,11 +208,23 @@ def test_decode_fp8_subnormal_k_codes_visible():
 # decode parity
 # ---------------------------------------------------------------------------
 
-def run_decode_fp8(w, partition=0):
+def midpoint_patterns(scale: float) -> np.ndarray:
+    """bf16 bit patterns whose fp32 quotient |x| / scale is exactly an E4M3
+    half-way point (numpy's correctly rounded fp32 division)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore", over="ignore"):
+        x = oracle.widen(bits, "bf16")
+        y32 = np.abs(x.astype(np.float32)) / np.float32(scale)
+    vals = oracle.fp8.E4M3_VALUES[:0x7F]
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    return bits[np.isfinite(x) & np.isin(y32, mids)]
+
+
+def run_decode_fp8(w, partition=0, t=None, check_oracle=True):
     """Store+decode (two calls) and fused store+decode on the same inputs,
     against the oracle. Returns the max error."""
     import torch
-    t = wl.make_host_tensors(w)
+    t = wl.make_host_tensors(w) if t is None else t
     hq, hkv, d, b = w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_seqs
     qkv = to_device(t["qkv"], "bf16")
     q = qkv[:, : hq * d].view(b, hq, d)
@@ -233,9 +252,31 @@ def run_decode_fp8(w, partition=0):
     assert np.array_equal(_codes(kc2), kc) and np.array_equal(_codes(vc2), vc)
     assert torch.all(full[0] == 7.0) and torch.all(full[b + 1] == 7.0), "write outside out"
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16)), "fused != store + decode"
+    if not check_oracle:
+        return None
     ref = oracle.decode(t["q"], kc, vc, w.block_tables, w.context_lens, w.scale, "bf16",
                         kv_dtype="fp8e4m3", k_scale=w.k_scale, v_scale=w.v_scale)
     return assert_attention_close(widen_host(to_host(out1, "bf16"), "bf16"), ref, "bf16", w.name)
+
+
+def test_store_decode_fp8_midpoint_quotients():
+    """New rows made of bf16 inputs whose fp32 quotient is an E4M3 half-way
+    point while the exact one is not: the plain store and the fused call's
+    quantiser give the oracle's codes (the exact quotient's), and the fused
+    output equals the two calls' bit for bit. (The rows hold values up to a
+    few hundred, so the attention outputs are compared with each other, not
+    with the oracle's tolerance; other tests cover that.)"""
+    k_scale, v_scale = 16 / 19, 1 / 3
+    w = wl.with_fp8_cache(wl.custom_decode([5, 17, 33, 64, 1], block_size=16, num_q_heads=8,
+                                           num_kv_heads=2, head_dim=128, dtype="bf16", seed=77),
+                          k_scale, v_scale)
+    t = wl.make_host_tensors(w)
+    pk, pv = midpoint_patterns(k_scale), midpoint_patterns(v_scale)
+    assert len(pk) >= 20 and len(pv) >= 20
+    n = t["k"].size
+    t["k"][...] = np.resize(pk, n).reshape(t["k"].shape)
+    t["v"][...] = np.resize(pv, n).reshape(t["v"].shape)
+    run_decode_fp8(w, 0, t=t, check_oracle=False)
 
 
 @pytest.mark.parametrize("partition", [0, 64])
@@ -264,30 +305,34 @@ def test_decode_fp8_small_scale_many_subnormals():
     run_decode_fp8(wl.with_fp8_cache(w, 8.0, 8.0), 64)
 
 
-def test_decode_fp8_full_size_sampled():
-    """qwen3-0.6b-decode-fp8 in the benchmark's launch configuration: fused
-    store+decode, sampled sequences checked against the oracle."""
+@pytest.mark.parametrize("name", ["qwen3-0.6b-decode-fp8", "long-context-decode-fp8"])
+def test_decode_fp8_full_size(name):
+    """The fp8 decode workloads in the benchmark's launch configuration:
+    fused store+decode into a NaN-filled output (every row must be written),
+    the quantised new rows at their slots, every sequence against the
+    oracle."""
     import torch
-    w = wl.DECODE_CONFIGS["qwen3-0.6b-decode-fp8"](0)
+    w = wl.DECODE_CONFIGS[name](0)
     print(f"[fp8-decode-full] {w.name} generating", flush=True)
     t = wl.make_device_tensors(w)
-    kc_h, vc_h = _codes(t["k_cache"]), _codes(t["v_cache"])
-    q_h, k_h, v_h = (to_host(t[x], "bf16") for x in ("q", "k", "v"))
-    out = binding.pa_store_decode_fp8(t["q"], t["k"], t["v"], torch.from_numpy(w.slot_mapping).cuda(),
-                                      t["k_cache"], t["v_cache"], torch.from_numpy(w.block_tables).cuda(),
-                                      torch.from_numpy(w.context_lens).cuda(), w.scale, w.k_scale,
-                                      w.v_scale)
+    snap = (t["k_cache"].clone(), t["v_cache"].clone())
+    slots = torch.from_numpy(w.slot_mapping).cuda()
+    out = fullsize.nan_out((w.num_seqs, w.num_q_heads, w.head_dim), torch.bfloat16)
+    binding.pa_store_decode_fp8(t["q"], t["k"], t["v"], slots, t["k_cache"], t["v_cache"],
+                                torch.from_numpy(w.block_tables).cuda(), torch.from_numpy(w.context_lens).cuda(),
+                                w.scale, w.k_scale, w.v_scale, out=out)
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(out.float()).all())
-    oracle.fp8.store_kvcache(oracle.widen(k_h, "bf16"), oracle.widen(v_h, "bf16"), kc_h, vc_h,
-                             w.slot_mapping, w.k_scale, w.v_scale)
-    assert np.array_equal(_codes(t["k_cache"]), kc_h) and np.array_equal(_codes(t["v_cache"]), vc_h)
-    seqs = [0, 1, int(np.argmax(w.context_lens)), int(np.argmin(w.context_lens)), w.num_seqs - 1]
-    ref = oracle.decode(q_h, kc_h, vc_h, w.block_tables, w.context_lens, w.scale, "bf16", seqs=seqs,
-                        kv_dtype="fp8e4m3", k_scale=w.k_scale, v_scale=w.v_scale)
+    assert bool(torch.isfinite(out.float()).all()), "a row was not written or a NaN code was read"
+    # the new rows' codes, from the oracle's quantiser
+    k_h, v_h = to_host(t["k"], "bf16"), to_host(t["v"], "bf16")
+    rows_k = t["k_cache"].view(-1, w.num_kv_heads, w.head_dim)[slots.long()]
+    rows_v = t["v_cache"].view(-1, w.num_kv_heads, w.head_dim)[slots.long()]
+    assert np.array_equal(_codes(rows_k), oracle.fp8.quantize(oracle.widen(k_h, "bf16"), w.k_scale))
+    assert np.array_equal(_codes(rows_v), oracle.fp8.quantize(oracle.widen(v_h, "bf16"), w.v_scale))
+    ref = fullsize.decode_reference(w, snap[0], snap[1], t["q"], t["k"], t["v"], list(range(w.num_seqs)))
     got = widen_host(to_host(out, "bf16"), "bf16")
-    err = assert_attention_close(got[seqs], ref[seqs], "bf16", "qwen3 fp8 sampled")
-    print(f"[fp8-decode-full] max err {err:.3e}", flush=True)
+    err = assert_attention_close(got, ref, "bf16", f"{w.name} all sequences")
+    print(f"[fp8-decode-full] {w.name}: all {w.num_seqs} sequences, max err {err:.3e}", flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -344,33 +389,31 @@ def test_prefill_fp8_block_sizes(bs, cached, sched):
     run_prefill_fp8(wl.with_fp8_cache(w, 0.02, 0.0125))
 
 
-def test_prefill_fp8_full_size_sampled():
+def test_prefill_fp8_full_size():
+    """chunked-prefill-fp8 in the benchmark's launch configuration: NaN-filled
+    output, stored codes bit for bit, and against the oracle every row of
+    sequence 0 plus one row of every query tile of the others."""
     import torch
     w = wl.PREFILL_CONFIGS["chunked-prefill-fp8"](0)
     print(f"[fp8-prefill-full] {w.name} generating", flush=True)
     t = wl.make_device_tensors(w)
     kc_h, vc_h = _codes(t["k_cache"]), _codes(t["v_cache"])
     q_h, k_h, v_h = (to_host(t[x], "bf16") for x in ("q", "k", "v"))
+    out = fullsize.nan_out((w.total_q, w.num_q_heads, w.head_dim), torch.bfloat16)
     binding.pa_store_kvcache_fp8(t["k"], t["v"], t["k_cache"], t["v_cache"],
                                  torch.from_numpy(w.slot_mapping).cuda(), w.k_scale, w.v_scale)
-    out = binding.pa_prefill_varlen_fp8(t["q"], t["k_cache"], t["v_cache"],
-                                        torch.from_numpy(w.cu_seqlens_q).cuda(),
-                                        torch.from_numpy(w.cu_seqlens_k).cuda(), w.max_seqlen_q,
-                                        w.max_seqlen_k, torch.from_numpy(w.block_tables).cuda(), w.scale,
-                                        w.k_scale, w.v_scale)
+    binding.pa_prefill_varlen_fp8(t["q"], t["k_cache"], t["v_cache"], torch.from_numpy(w.cu_seqlens_q).cuda(),
+                                  torch.from_numpy(w.cu_seqlens_k).cuda(), w.max_seqlen_q, w.max_seqlen_k,
+                                  torch.from_numpy(w.block_tables).cuda(), w.scale, w.k_scale, w.v_scale,
+                                  out=out)
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(out.float()).all())
+    assert bool(torch.isfinite(out.float()).all()), "a query row was not written"
     oracle.fp8.store_kvcache(oracle.widen(k_h, "bf16"), oracle.widen(v_h, "bf16"), kc_h, vc_h,
                              w.slot_mapping, w.k_scale, w.v_scale)
     assert np.array_equal(_codes(t["k_cache"]), kc_h) and np.array_equal(_codes(t["v_cache"]), vc_h)
-    rng = np.random.default_rng(4)
-    rows = []
-    for i in range(w.num_seqs):
-        q0, q1 = int(w.cu_seqlens_q[i]), int(w.cu_seqlens_q[i + 1])
-        rows += [q0, q1 - 1, int(rng.integers(q0, q1))]
-    rows = sorted(set(rows))
-    ref = oracle.prefill_varlen(q_h, kc_h, vc_h, w.cu_seqlens_q, w.cu_seqlens_k, w.block_tables, w.scale,
-                                "bf16", rows=rows, kv_dtype="fp8e4m3", k_scale=w.k_scale, v_scale=w.v_scale)
+    g = w.num_q_heads // w.num_kv_heads
+    rows = fullsize.prefill_rows_per_tile(w, 128 // g, full_seqs=(0,))
+    ref = fullsize.prefill_reference(w, q_h, kc_h, vc_h, rows)
     got = widen_host(to_host(out, "bf16"), "bf16")
-    err = assert_attention_close(got[rows], ref[rows], "bf16", "chunked-prefill fp8 sampled rows")
+    err = assert_attention_close(got[rows], ref[rows], "bf16", "chunked-prefill fp8 rows")
     print(f"[fp8-prefill-full] {len(rows)} rows, max err {err:.3e}", flush=True)
