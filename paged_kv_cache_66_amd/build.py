@@ -2,7 +2,9 @@
 
 Every source is compiled with hipcc for gfx950 only, with packed-fp32 VALU
 instructions disabled, then linked into one shared library next to this
-file. Run as ``python -m paged_kv_cache_66_amd.build``.
+file. The SHA-256 of the sources (``srchash.source_sha256``) is written to a
+generated header in the build folder and baked into ``pa_version()``. Run as
+``python -m paged_kv_cache_66_amd.build``.
 """
 from __future__ import annotations
 
@@ -11,6 +13,12 @@ import shutil
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
+
+if __package__ in (None, ""):
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    from paged_kv_cache_66_amd.srchash import source_sha256
+else:
+    from .srchash import source_sha256
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -41,7 +49,8 @@ COMMON_FLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-I", CSRC, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, "-I", CSRC, "-I", INCLUDE, "-I", BUILD_DIR, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
@@ -51,6 +60,9 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     """Compile all sources and link ``libpa.so``; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
+    digest = source_sha256()
+    with open(os.path.join(BUILD_DIR, "pa_srchash.h"), "w") as f:
+        f.write(f'#define PA_SOURCE_SHA256 "{digest}"\n')
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB_PATH + ".tmp"
@@ -60,7 +72,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} (src-sha256:{digest})")
     return LIB_PATH
 
 

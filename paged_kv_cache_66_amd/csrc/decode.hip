@@ -184,8 +184,8 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
     void* __restrict__ out, const char* __restrict__ q, int64_t q_stride_bytes,
     char* __restrict__ k_cache, char* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, int32_t max_blocks,
-    const int32_t* __restrict__ context_lens, int32_t num_q_heads, int32_t num_kv_heads,
-    int32_t log2_bs, float scale_log2, int32_t partition, int32_t num_partitions,
+    const int32_t* __restrict__ context_lens, int32_t max_ctx, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t log2_bs, float scale_log2, int32_t partition, int32_t num_partitions,
     int32_t score_words, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
     const char* __restrict__ new_k, int64_t new_k_stride_bytes, const char* __restrict__ new_v,
     int64_t new_v_stride_bytes, const int32_t* __restrict__ slot_mapping, float k_scale,
@@ -239,7 +239,8 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   const int grp = lane / LPT;
   const int li = lane % LPT;
 
-  const int n = context_lens[b];
+  // a history never runs past its table row (max_ctx = max_blocks * block_size)
+  const int n = min(context_lens[b], max_ctx);
   const int t0 = p * partition;
   const bool single = (num_partitions == 1);
   if (t0 >= n) {
@@ -505,14 +506,14 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 template <typename T, int D>
 __global__ void __launch_bounds__(64) decode_reduce_kernel(
     void* __restrict__ out, const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
-    const int32_t* __restrict__ context_lens, int32_t num_q_heads, int32_t partition,
-    int32_t num_partitions) {
+    const int32_t* __restrict__ context_lens, int32_t max_ctx, int32_t num_q_heads,
+    int32_t partition, int32_t num_partitions) {
   constexpr int PER = D / 64;
   constexpr int kBatch = 8;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int lane = threadIdx.x;
-  const int n = context_lens[b];
+  const int n = min(context_lens[b], max_ctx);  // as in the partition kernel
   const int np = (n + partition - 1) / partition;
   const int64_t slot0 = (static_cast<int64_t>(b) * num_q_heads + h) * num_partitions;
   const float* ml = ws_ml + slot0 * 2;
@@ -568,12 +569,14 @@ hipError_t launch_decode_typed(const DecodeArgs& a, hipStream_t stream) {
   const size_t lds = static_cast<size_t>(new_words + score_words + 2 * G + max_ids) * 4;
   // an E4M3 cache holds K / k_scale: the score scale absorbs k_scale
   const float scale_log2 = a.scale * (Elem<T>::kBytes == 1 ? a.k_scale : 1.f) * kLog2e;
+  const int64_t table_rows = static_cast<int64_t>(a.max_blocks) << log2_bs;
+  const int32_t max_ctx = static_cast<int32_t>(table_rows < INT32_MAX ? table_rows : INT32_MAX);
   dim3 grid(a.num_partitions * a.num_kv_heads * a.num_seqs);
   hipLaunchKernelGGL((decode_partition_kernel<T, D, G, FUSED>), grid, dim3(kThreads), lds, stream,
                      a.out, static_cast<const char*>(a.q), a.q_stride * QB,
                      static_cast<char*>(const_cast<void*>(a.k_cache)),
                      static_cast<char*>(const_cast<void*>(a.v_cache)), a.block_tables, a.max_blocks,
-                     a.context_lens, a.num_q_heads, a.num_kv_heads, log2_bs, scale_log2, a.partition,
+                     a.context_lens, max_ctx, a.num_q_heads, a.num_kv_heads, log2_bs, scale_log2, a.partition,
                      a.num_partitions, score_words, a.ws_acc, a.ws_ml,
                      static_cast<const char*>(a.new_k), a.new_k_stride * QB,
                      static_cast<const char*>(a.new_v), a.new_v_stride * QB, a.slot_mapping,
@@ -581,8 +584,8 @@ hipError_t launch_decode_typed(const DecodeArgs& a, hipStream_t stream) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.num_partitions == 1) return err;
   hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3(a.num_q_heads, a.num_seqs), dim3(64), 0,
-                     stream, a.out, a.ws_acc, a.ws_ml, a.context_lens, a.num_q_heads, a.partition,
-                     a.num_partitions);
+                     stream, a.out, a.ws_acc, a.ws_ml, a.context_lens, max_ctx, a.num_q_heads,
+                     a.partition, a.num_partitions);
   return hipGetLastError();
 }
 

@@ -10,6 +10,13 @@
 
 #include "pa_internal.h"
 
+// The build writes the SHA-256 of the library's sources into this header.
+#if __has_include("pa_srchash.h")
+#include "pa_srchash.h"
+#else
+#define PA_SOURCE_SHA256 "unknown"
+#endif
+
 namespace {
 
 constexpr int32_t kMaxBlockSize = 1024;
@@ -291,7 +298,9 @@ const char* pa_status_string(int status) {
   }
 }
 
-const char* pa_version(void) { return "paged_kv_cache_66_amd 0.1.0 (gfx950)"; }
+const char* pa_version(void) {
+  return "paged_kv_cache_66_amd 0.2.0 (gfx950) src-sha256:" PA_SOURCE_SHA256;
+}
 
 pa_status pa_store_kvcache(const void* key, int64_t key_row_stride, const void* value,
                            int64_t value_row_stride, void* k_cache, void* v_cache,

@@ -271,6 +271,14 @@ __device__ __forceinline__ void tile_of_workgroup(int L, int num_kv_heads, int m
 // r of the workgroup's 128 is query head g * G + r / QT at query q_lo + r % QT
 // (heads of the group packed together), with its absolute position and its
 // output row (-1 for padding columns past the chunk).
+// Keys a sequence's attention reads: Lk, cut in paged mode to the rows its
+// block-table row can name (max_blocks << log2_bs), so no tile walks past the
+// row whatever cu_seqlens_k says.
+__device__ __forceinline__ int clamp_keys(int lk, bool paged, int max_blocks, int log2_bs) {
+  const int64_t rows = static_cast<int64_t>(max_blocks) << log2_bs;
+  return paged && lk > rows ? static_cast<int>(rows) : lk;
+}
+
 template <int D, int G>
 __device__ __forceinline__ void load_q(const char* q, int64_t q_stride_bytes, int q0, int Lq, int q_lo,
                                        int start, int g, int wave, int col, int gq,
@@ -387,7 +395,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(
   tile_of_workgroup(blockIdx.x, num_kv_heads, max_qt, i, g, x);
   const int q0 = cu_q[i];
   const int Lq = cu_q[i + 1] - q0;
-  const int Lk = cu_k[i + 1] - cu_k[i];
+  // paged keys never run past the sequence's table row
+  const int Lk = clamp_keys(cu_k[i + 1] - cu_k[i], block_tables != nullptr, max_blocks, log2_bs);
   const int n_qt = (Lq + QT - 1) / QT;
   if (x >= n_qt) return;
   const int qt = n_qt - 1 - x;  // heaviest tiles first
@@ -642,7 +651,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_direct_kernel(
   tile_of_workgroup(blockIdx.x, num_kv_heads, max_qt, i, g, x);
   const int q0 = cu_q[i];
   const int Lq = cu_q[i + 1] - q0;
-  const int Lk = cu_k[i + 1] - cu_k[i];
+  // paged keys never run past the sequence's table row
+  const int Lk = clamp_keys(cu_k[i + 1] - cu_k[i], block_tables != nullptr, max_blocks, log2_bs);
   const int n_qt = (Lq + QT - 1) / QT;
   if (x >= n_qt) return;
   const int qt = n_qt - 1 - x;  // heaviest tiles first

@@ -3,15 +3,16 @@
     python3 -m paged_kv_cache_66_amd.profile_summary stats OUT/run_kernel_stats.csv
     python3 -m paged_kv_cache_66_amd.profile_summary pmc OUT/run_counter_collection.csv
     python3 -m paged_kv_cache_66_amd.profile_summary traffic KFETCH KWRITE CFETCH CWRITE \
-        COPY_BYTES SOURCE NAME...
+        COPY_BYTES KIND NAME...
 
 `stats` lists per-kernel call counts and durations; `pmc` averages every
 collected counter per kernel over its dispatches. `traffic` turns FETCH_SIZE
 and WRITE_SIZE runs (KiB per dispatch) of the kernels whose names contain one
 of NAME... into HBM bytes per launch of the whole call, each counter scaled
 by the ratio of known bytes to what the same counter read for a plain copy
-of COPY_BYTES bytes, and stamps the result with the SHA-256 of SOURCE (the
-figure is stale once that file changes). Kernel names are shortened to the
+of COPY_BYTES bytes, and stamps the result with the SHA-256 of the sources
+of kernel family KIND ("decode", "prefill" or "store": srchash.kernel_sha256;
+the figure is stale once one of them changes). Kernel names are shortened to the
 function name with template arguments.
 """
 from __future__ import annotations
@@ -65,9 +66,12 @@ def _per_dispatch(path: str, counter: str, names) -> dict:
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
-def traffic(kfetch, kwrite, cfetch, cwrite, copy_bytes, source, names) -> dict:
-    import hashlib
-    import json  # noqa: F401
+def traffic(kfetch, kwrite, cfetch, cwrite, copy_bytes, kind, names) -> dict:
+    if __package__ in (None, ""):
+        sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+        from paged_kv_cache_66_amd.srchash import KERNEL_SOURCES, kernel_sha256
+    else:
+        from .srchash import KERNEL_SOURCES, kernel_sha256
 
     cf = _per_dispatch(cfetch, "FETCH_SIZE", ["copy"])
     cw = _per_dispatch(cwrite, "WRITE_SIZE", ["copy"])
@@ -78,11 +82,9 @@ def traffic(kfetch, kwrite, cfetch, cwrite, copy_bytes, source, names) -> dict:
     per_kernel = {k: {"fetch_bytes": kf.get(k, 0) * 1024 * fetch_factor,
                       "write_bytes": kw.get(k, 0) * 1024 * write_factor} for k in sorted(set(kf) | set(kw))}
     total = sum(v["fetch_bytes"] + v["write_bytes"] for v in per_kernel.values())
-    with open(source, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
     return {"bytes_per_launch": round(total), "fetch_factor": round(fetch_factor, 4),
             "write_factor": round(write_factor, 4), "per_kernel": per_kernel,
-            "kernel_sha256": sha, "source": os.path.basename(source)}
+            "kernel_sha256": kernel_sha256(kind), "kernel_sources": KERNEL_SOURCES[kind]}
 
 
 def main(argv=None):

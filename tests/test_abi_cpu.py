@@ -9,7 +9,8 @@ import pytest
 
 from paged_kv_cache_66_amd import binding
 
-OK, NULL, SHAPE, UNSUP, ALIGN, WS = 0, 1, 2, 3, 4, 5
+# pa_status codes, fixed by include/pa.h (test_status_codes_match_header)
+OK, NULL, SHAPE, UNSUP, WS, HIP, ALIGN = 0, 1, 2, 3, 4, 5, 6
 F32, BF16 = 0, 1
 A = 1 << 20  # a 16-byte aligned fake device address: never dereferenced on these paths
 
@@ -37,11 +38,38 @@ def test_exports_every_header_symbol(lib):
         assert hasattr(lib, n)
 
 
+def test_status_codes_match_header(lib):
+    import re
+    with open(binding.HEADER) as f:
+        text = f.read()
+    enum = re.search(r"typedef enum pa_status \{(.*?)\} pa_status;", text, re.S).group(1)
+    codes = {m.group(1): int(m.group(2)) for m in re.finditer(r"(PA_\w+)\s*=\s*(\d+)", enum)}
+    assert codes == {"PA_OK": OK, "PA_ERR_NULL": NULL, "PA_ERR_SHAPE": SHAPE,
+                     "PA_ERR_UNSUPPORTED": UNSUP, "PA_ERR_WORKSPACE": WS, "PA_ERR_HIP": HIP,
+                     "PA_ERR_ALIGN": ALIGN}
+    assert {v: k for k, v in codes.items()} == binding.STATUS
+
+
 def test_status_strings(lib):
-    for s in range(7):
-        assert lib.pa_status_string(s)
+    expect = {OK: b"ok", NULL: b"null", SHAPE: b"size", UNSUP: b"unsupported", WS: b"workspace",
+              HIP: b"HIP", ALIGN: b"aligned"}
+    for code, word in expect.items():
+        assert word in lib.pa_status_string(code), code
     assert b"unknown" in lib.pa_status_string(99)
+    assert b"unknown" in lib.pa_status_string(-1)
     assert b"gfx950" in lib.pa_version()
+
+
+def test_library_built_from_this_tree(lib):
+    """pa_version() carries the SHA-256 of the sources the library was built
+    from; it must be this tree's."""
+    from paged_kv_cache_66_amd import srchash
+    got = binding.library_source_sha256()
+    assert len(got) == 64 and got == srchash.source_sha256(), (got, srchash.source_sha256())
+    assert binding.check_source_hash() == got
+    files = srchash.source_files()
+    assert files[0] == "include/pa.h" and files == sorted(files)
+    assert any(f.endswith("decode.hip") for f in files) and any(f.endswith("pa_api.cpp") for f in files)
 
 
 def store(lib, **kw):
