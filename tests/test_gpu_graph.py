@@ -4,8 +4,10 @@ bucket 1, 2, 4, 8, ...; before replay the runner copies the step's inputs into
 static buffers, fills slot_mapping with -1 and zeroes context_lens for the
 padding rows).
 
-pa_store_kvcache + pa_decode are captured once per bucket with static
-buffers and replayed over several steps with changing contents. Every replay
+pa_store_kvcache + pa_decode (or the fused pa_store_decode) are captured
+once per bucket with static buffers and replayed over several steps with
+changing contents; buckets run from 1 to 512 (the large-batch decode
+workload's head shapes for the smallest and largest). Every replay
 is compared bit for bit with the same two calls run eagerly on a copy of the
 cache state, and with the fp64 oracle; padding rows must leave the cache
 untouched and produce zero output rows. Between replays the test runs its own
@@ -33,11 +35,20 @@ def _step_inputs(rng, ctx, tables, bs, hq, hkv, d):
     return q, k, v, slots, np.asarray(ctx, np.int32)
 
 
-@pytest.mark.parametrize("bucket,real", [(8, 5), (4, 4), (16, 9)])
-def test_graph_replay_matches_eager(bucket, real):
+SMALL_HEADS = (8, 2)    # H_q, H_kv
+HEADS_8B = (32, 8)      # the large-batch decode workload's heads
+
+
+@pytest.mark.parametrize("bucket,real,heads,fused", [
+    (8, 5, SMALL_HEADS, False), (4, 4, SMALL_HEADS, False), (16, 9, SMALL_HEADS, False),
+    (1, 1, HEADS_8B, False), (1, 1, HEADS_8B, True),          # the smallest bucket
+    (512, 300, HEADS_8B, False), (512, 300, HEADS_8B, True),  # the largest bucket, mostly real rows
+])
+def test_graph_replay_matches_eager(bucket, real, heads, fused):
     import torch
-    hq, hkv, d, bs = 8, 2, 128, 16
-    rng = np.random.default_rng(bucket * 100 + real)
+    hq, hkv = heads
+    d, bs = 128, 16
+    rng = np.random.default_rng(bucket * 100 + real + 7 * fused)
     steps = 3
     # sequences grow by one token per step; reserve blocks for every step
     ctx0 = [int(x) for x in rng.integers(20, 120, size=real)]
@@ -78,6 +89,10 @@ def test_graph_replay_matches_eager(bucket, real):
         ctx_s[:real].copy_(torch.from_numpy(ctx).cuda())
 
     def step_calls(kcache, vcache, out):
+        if fused:
+            binding.pa_store_decode(q_s, k_s, v_s, slots_s, kcache, vcache, tables_s, ctx_s, scale, out=out,
+                                    workspace=ws, partition_size=64)
+            return
         binding.pa_store_kvcache(k_s, v_s, kcache, vcache, slots_s)
         binding.pa_decode(q_s, kcache, vcache, tables_s, ctx_s, scale, out=out, workspace=ws,
                           partition_size=64)
@@ -92,7 +107,7 @@ def test_graph_replay_matches_eager(bucket, real):
         step_calls(kw, vw, torch.empty_like(out_s))
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    print(f"[graph] capture bucket={bucket} real={real}", flush=True)
+    print(f"[graph] capture bucket={bucket} real={real} heads={heads} fused={fused}", flush=True)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step_calls(kc_d, vc_d, out_s)

@@ -3,14 +3,16 @@ pa_prefill_varlen through the block tables) against the fp64 oracle:
 element by element on small varlen batches (mid-block chunk starts, chunks
 spanning several 128-row query tiles and 64-key tiles with ragged tails,
 shared prefix blocks, every group size and both head dims, block sizes 4..256)
-and on sampled rows of the full 16384-token chunked-prefill workload in the
-launch configuration the benchmark times."""
+and on the full 16384-token chunked-prefill workload in the launch
+configuration the benchmark times (NaN-filled output; every row of one
+sequence and one row of every query tile against the oracle)."""
 import numpy as np
 import pytest
 
 import oracle
 from paged_kv_cache_66_amd import binding
 from paged_kv_cache_66_amd import workloads as wl
+from tests import fullsize
 from tests.helpers import assert_attention_close, gpu_available, to_device, to_host, widen_host
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -114,7 +116,12 @@ def test_prefill_small_chunked_config():
     run_small(w)
 
 
-def test_full_chunked_prefill_sampled():
+def test_full_chunked_prefill():
+    """The chunked-prefill workload in the benchmark's launch configuration:
+    a NaN-filled output (every row must be written), the stored rows bit for
+    bit, and against the oracle every row of sequence 0 (its chunk starts
+    inside a block) plus one row of every query tile (128 / G queries per
+    workgroup) and the first and last row of every other sequence."""
     import torch
     w = wl.chunked_prefill(seed=0)
     print(f"[prefill-full] {w.name} {w.note} generating", flush=True)
@@ -126,28 +133,24 @@ def test_full_chunked_prefill_sampled():
     k_h = to_host(t["k"], w.dtype)
     v_h = to_host(t["v"], w.dtype)
     print("[prefill-full] store + prefill", flush=True)
+    out = fullsize.nan_out((w.total_q, w.num_q_heads, w.head_dim), t["q"].dtype)
     binding.pa_store_kvcache(t["k"], t["v"], t["k_cache"], t["v_cache"],
                              torch.from_numpy(w.slot_mapping).cuda())
-    out = binding.pa_prefill_varlen(t["q"], t["k_cache"], t["v_cache"],
-                                    torch.from_numpy(w.cu_seqlens_q).cuda(),
-                                    torch.from_numpy(w.cu_seqlens_k).cuda(), w.max_seqlen_q,
-                                    w.max_seqlen_k, torch.from_numpy(w.block_tables).cuda(), w.scale)
+    binding.pa_prefill_varlen(t["q"], t["k_cache"], t["v_cache"], torch.from_numpy(w.cu_seqlens_q).cuda(),
+                              torch.from_numpy(w.cu_seqlens_k).cuda(), w.max_seqlen_q, w.max_seqlen_k,
+                              torch.from_numpy(w.block_tables).cuda(), w.scale, out=out)
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(out.float()).all())
+    assert bool(torch.isfinite(out.float()).all()), "a query row was not written"
     oracle.store_kvcache(k_h, v_h, kc_h, vc_h, w.slot_mapping)
     assert np.array_equal(to_host(t["k_cache"], w.dtype), kc_h)
     assert np.array_equal(to_host(t["v_cache"], w.dtype), vc_h)
-    rng = np.random.default_rng(4)
-    rows = []
-    for i in range(w.num_seqs):
-        q0, q1 = int(w.cu_seqlens_q[i]), int(w.cu_seqlens_q[i + 1])
-        rows += [q0, q1 - 1, (q0 + q1) // 2, int(rng.integers(q0, q1))]
-    rows = sorted(set(rows))
-    ref = oracle.prefill_varlen(q_h, kc_h, vc_h, w.cu_seqlens_q, w.cu_seqlens_k, w.block_tables,
-                                w.scale, w.dtype, rows=rows)
+    g = w.num_q_heads // w.num_kv_heads
+    rows = fullsize.prefill_rows_per_tile(w, 128 // g, full_seqs=(0,))
+    ref = fullsize.prefill_reference(w, q_h, kc_h, vc_h, rows)
     got = widen_host(to_host(out, w.dtype), w.dtype)
-    err = assert_attention_close(got[rows], ref[rows], w.dtype, "chunked-prefill sampled rows")
-    print(f"[prefill-full] {len(rows)} sampled rows, max err {err:.3e}", flush=True)
+    err = assert_attention_close(got[rows], ref[rows], w.dtype, "chunked-prefill rows")
+    print(f"[prefill-full] {len(rows)} rows (all of sequence 0, one per query tile), max err {err:.3e}",
+          flush=True)
 
 
 # ---------------------------------------------------------------------------

@@ -34,7 +34,8 @@ def _fused_vs_separate(w, d, fp8):
     cuk = torch.from_numpy(w.cu_seqlens_k).cuda()
     kc2, vc2 = d["k_cache"].clone(), d["v_cache"].clone()
     tq = w.total_q
-    full = torch.full((tq + 2, w.num_q_heads, w.head_dim), 3.0, dtype=torch.bfloat16, device="cuda")
+    # NaN-filled: every row must be written; guard rows around it must not be
+    full = torch.full((tq + 2, w.num_q_heads, w.head_dim), float("nan"), dtype=torch.bfloat16, device="cuda")
     fused = full[1:tq + 1]
     print(f"[store-prefill] {w.name} cached={w.num_cached.tolist()[:8]} sched={w.num_scheduled.tolist()[:8]} "
           f"Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} bs={w.block_size} fp8={fp8}", flush=True)
@@ -51,7 +52,8 @@ def _fused_vs_separate(w, d, fp8):
         binding.pa_store_prefill(d["q"], d["k"], d["v"], slots, kc2, vc2, cuq, cuk, w.max_seqlen_q,
                                  w.max_seqlen_k, tables, w.scale, out=fused)
     torch.cuda.synchronize()
-    assert torch.all(full[0] == 3.0) and torch.all(full[tq + 1] == 3.0), "write outside out"
+    assert torch.all(torch.isnan(full[0])) and torch.all(torch.isnan(full[tq + 1])), "write outside out"
+    assert bool(torch.isfinite(fused.float()).all()), "a fused output row was not written"
     assert torch.equal(sep.view(torch.int16), fused.view(torch.int16)), "fused output differs"
     cv = torch.uint8 if fp8 else torch.int16
     assert torch.equal(d["k_cache"].view(cv), kc2.view(cv)), "fused K scatter differs"
