@@ -20,7 +20,8 @@
  * ---------------------------------------
  * Ownership.  Every pointer argument is a device pointer owned by the caller
  *   (typically a torch tensor's data_ptr()). The library allocates no device
- *   memory and keeps no mutable global state. Work is enqueued
+ *   memory and keeps no mutable global state, except the fixed workspace
+ *   array of pa_store_decode_noalloc (declared with it). Work is enqueued
  *   asynchronously on `stream` (a hipStream_t; NULL = the default stream);
  *   the caller keeps the buffers alive until the stream has passed them. No
  *   call reads device memory on the host or synchronises, so every call can
@@ -218,6 +219,35 @@ pa_status pa_store_decode(void* out, const void* q, int64_t q_row_stride, const 
                           int32_t num_blocks, float scale, int32_t partition_size,
                           pa_dtype dtype, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * pa_store_decode_noalloc - pa_store_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the split-K workspace is not passed in but lives in
+ * a fixed device array inside the library, PA_NOALLOC_WORKSPACE_BYTES (64 MiB)
+ * per GPU, held from the first call on that GPU until the process ends. The
+ * call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); its first call on a GPU looks the array's address up once.
+ *
+ * Same arguments, preconditions and result (bit for bit) as pa_store_decode
+ * without the workspace arguments. A launch whose workspace
+ * (pa_decode_workspace_size of the same sizes) exceeds the array returns
+ * PA_ERR_WORKSPACE and enqueues nothing; pick a longer partition_size or
+ * fewer sequences per call. Every call on one GPU shares that GPU's array:
+ * calls whose kernels overlap in time on one GPU (different streams, or
+ * host threads) race on it and must be serialised by the caller; calls in
+ * order on one stream, or captured in one graph, are safe. The array keeps
+ * the last call's partials; nothing in it needs clearing between calls.
+ */
+#define PA_NOALLOC_WORKSPACE_BYTES (64u << 20)
+pa_status pa_store_decode_noalloc(void* out, const void* q, int64_t q_row_stride, const void* key,
+                                  int64_t key_row_stride, const void* value, int64_t value_row_stride,
+                                  const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, float scale, int32_t partition_size,
+                                  pa_dtype dtype, void* stream);
 
 /*
  * pa_prefill_varlen - packed varlen causal prefill ("Inference Engine Inside

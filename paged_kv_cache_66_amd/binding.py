@@ -42,6 +42,9 @@ _SIGNATURES = {
     "pa_store_decode": (ctypes.c_int, [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i32,
                                        _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                        ctypes.c_int, _vp, _sz, _vp]),
+    "pa_store_decode_noalloc": (ctypes.c_int, [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp,
+                                               _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                               ctypes.c_int, _vp]),
     "pa_prefill_varlen": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _i64, _vp, _i64, _vp, _vp, _i32,
                                          _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                          _f32, ctypes.c_int, _vp]),
@@ -255,6 +258,36 @@ def pa_store_decode(q, key, value, slot_mapping, k_cache, v_cache, block_tables,
                              context_lens.data_ptr(), b, hq, hkv, d, bs, n, float(scale),
                              int(partition_size), _dtype_code(q), wp, wn, _stream(q))
     _check("pa_store_decode", st)
+    return out
+
+
+def pa_store_decode_noalloc(q, key, value, slot_mapping, k_cache, v_cache, block_tables, context_lens,
+                            scale, out, partition_size=0):
+    """pa_store_decode with the split-K workspace in the library's fixed
+    device array (PA_NOALLOC_WORKSPACE_BYTES per GPU): nothing is allocated,
+    so ``out`` [B, H_q, D] must be given."""
+    lib = load()
+    n, bs, hkv, d = _cache_dims(k_cache, v_cache)
+    _int32(block_tables, "block_tables")
+    _int32(context_lens, "context_lens")
+    _int32(slot_mapping, "slot_mapping")
+    qp, qs = _rows(q, "q")
+    kp, ks = _rows(key, "key")
+    vp, vs = _rows(value, "value")
+    b, hq = int(q.shape[0]), int(q.shape[1])
+    _require(q.shape[2] == d and q.dtype == k_cache.dtype, "q shape/dtype")
+    _require(tuple(key.shape) == (b, hkv, d) and tuple(value.shape) == (b, hkv, d), "key/value shape")
+    _require(key.dtype == value.dtype == k_cache.dtype, "key/value dtype")
+    _require(slot_mapping.shape == (b,), "slot_mapping must be [B]")
+    _require(block_tables.dim() == 2 and block_tables.shape[0] == b, "block_tables must be [B, W]")
+    _require(context_lens.shape == (b,), "context_lens must be [B]")
+    _require(out is not None and out.is_contiguous() and tuple(out.shape) == (b, hq, d) and
+             out.dtype == q.dtype, "out [B, H_q, D] must be given (this call allocates nothing)")
+    st = lib.pa_store_decode_noalloc(out.data_ptr(), qp, qs, kp, ks, vp, vs, slot_mapping.data_ptr(),
+                                     k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+                                     int(block_tables.shape[1]), context_lens.data_ptr(), b, hq, hkv, d, bs, n,
+                                     float(scale), int(partition_size), _dtype_code(q), _stream(q))
+    _check("pa_store_decode_noalloc", st)
     return out
 
 

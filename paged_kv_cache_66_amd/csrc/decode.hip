@@ -32,6 +32,8 @@
 // A second kernel merges the partials of a (sequence, query head) with the
 // log-sum-exp rule. Summation order depends only on logical positions, so
 // the result is bitwise independent of where blocks sit in the pool.
+#include <mutex>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -658,6 +660,33 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
                               : dispatch_fused<float, 128>(a, stream);
   }
   return hipErrorInvalidValue;
+}
+
+// Split-K workspace of pa_store_decode_noalloc, for callers that cannot
+// allocate: a fixed device array, one copy per GPU, kept until the process
+// ends. Host code never passes `scratch` itself to a kernel (on the host the
+// name is a stand-in, not a device address): each device's address comes
+// from hipGetSymbolAddress, called once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[kStaticWorkspaceBytes];
+
+hipError_t static_workspace(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace pa

@@ -94,7 +94,7 @@ pa_status prepare_decode(void* out, const void* q, int64_t q_row_stride, const v
                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                          int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
                          int32_t partition_size, pa_dtype dtype, pa::KvFormat kv, float k_scale,
-                         float v_scale, void* workspace, size_t workspace_bytes,
+                         float v_scale, void* workspace, size_t workspace_bytes, bool static_ws,
                          pa::DecodeArgs* a) {
   if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
   if (kv == pa::KvFormat::kFp8E4m3 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
@@ -129,10 +129,16 @@ pa_status prepare_decode(void* out, const void* q, int64_t q_row_stride, const v
   if (P > 1) {
     const size_t need = pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                  block_size, max_blocks_per_seq, partition_size);
-    if (workspace == nullptr || workspace_bytes < need) return PA_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return PA_ERR_ALIGN;
-    ws_acc = static_cast<float*>(workspace);
-    ws_ml = ws_acc + static_cast<int64_t>(num_seqs) * num_q_heads * P * head_dim;
+    if (static_ws) {
+      // the library's fixed array, whose address the caller resolves once
+      // every check has passed: only its size is checked here
+      if (need > pa::kStaticWorkspaceBytes) return PA_ERR_WORKSPACE;
+    } else {
+      if (workspace == nullptr || workspace_bytes < need) return PA_ERR_WORKSPACE;
+      if (!aligned16(workspace)) return PA_ERR_ALIGN;
+      ws_acc = static_cast<float*>(workspace);
+      ws_ml = ws_acc + static_cast<int64_t>(num_seqs) * num_q_heads * P * head_dim;
+    }
   }
   *a = pa::DecodeArgs{};
   a->out = out;
@@ -167,13 +173,14 @@ pa_status decode_common(void* out, const void* q, int64_t q_row_stride, const vo
                         int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                         int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
                         int32_t partition_size, pa_dtype dtype, pa::KvFormat kv, float k_scale,
-                        float v_scale, void* workspace, size_t workspace_bytes, void* stream) {
+                        float v_scale, void* workspace, size_t workspace_bytes, void* stream,
+                        bool static_ws = false) {
   pa::DecodeArgs a;
   pa_status st = prepare_decode(out, q, q_row_stride, k_cache, v_cache, block_tables,
                                 max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
                                 num_kv_heads, head_dim, block_size, num_blocks, scale,
                                 partition_size, dtype, kv, k_scale, v_scale, workspace,
-                                workspace_bytes, &a);
+                                workspace_bytes, static_ws, &a);
   if (st != PA_OK || num_seqs == 0) return st;
   if (fused) {
     if (key == nullptr || value == nullptr || slot_mapping == nullptr) return PA_ERR_NULL;
@@ -181,6 +188,15 @@ pa_status decode_common(void* out, const void* q, int64_t q_row_stride, const vo
     const int64_t row = static_cast<int64_t>(num_kv_heads) * head_dim;
     if ((st = check_rows(key, key_row_stride, row, eb)) != PA_OK) return st;
     if ((st = check_rows(value, value_row_stride, row, eb)) != PA_OK) return st;
+  }
+  if (static_ws && a.num_partitions > 1) {
+    // every check has passed: resolve the fixed array's address on this device
+    void* ws = nullptr;
+    if (pa::static_workspace(&ws) != hipSuccess) return PA_ERR_HIP;
+    a.ws_acc = static_cast<float*>(ws);
+    a.ws_ml = a.ws_acc + static_cast<int64_t>(num_seqs) * num_q_heads * a.num_partitions * head_dim;
+  }
+  if (fused) {
     a.new_k = key;
     a.new_k_stride = key_row_stride;
     a.new_v = value;
@@ -368,6 +384,23 @@ pa_status pa_store_decode(void* out, const void* q, int64_t q_row_stride, const 
                        context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                        num_blocks, scale, partition_size, dtype, kv_of(dtype), 1.f, 1.f,
                        workspace, workspace_bytes, stream);
+}
+
+pa_status pa_store_decode_noalloc(void* out, const void* q, int64_t q_row_stride, const void* key,
+                                  int64_t key_row_stride, const void* value, int64_t value_row_stride,
+                                  const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, float scale, int32_t partition_size,
+                                  pa_dtype dtype, void* stream) {
+  // the split-K workspace is the library's fixed array (static_ws): looked
+  // up after every other check, refused when the launch needs more
+  return decode_common(out, q, q_row_stride, key, key_row_stride, value, value_row_stride,
+                       slot_mapping, true, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, scale, partition_size, dtype, kv_of(dtype), 1.f, 1.f, nullptr, 0,
+                       stream, /*static_ws=*/true);
 }
 
 pa_status pa_decode_fp8(void* out, const void* q, int64_t q_row_stride, const void* k_cache,

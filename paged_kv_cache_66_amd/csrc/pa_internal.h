@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pa.h"
+
 namespace pa {
 
 // Storage format of the K/V caches. fp32 and bf16 caches share the element
@@ -108,5 +110,11 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 int32_t decode_partition_tokens(int32_t requested, int32_t num_seqs, int32_t num_kv_heads,
                                 int32_t group, int32_t block_size, int32_t max_blocks,
                                 int32_t elem_bytes);
+
+// Fixed split-K workspace of the allocation-free decode entry point: its
+// size, and its device address on the current device (looked up once per
+// device; hipGetSymbolAddress allocates nothing).
+constexpr size_t kStaticWorkspaceBytes = PA_NOALLOC_WORKSPACE_BYTES;
+hipError_t static_workspace(void** ptr);
 
 }  // namespace pa

@@ -29,7 +29,7 @@ def test_exports_every_header_symbol(lib):
                           "pa_decode_workspace_size", "pa_decode", "pa_store_decode",
                           "pa_prefill_varlen", "pa_store_kvcache_fp8", "pa_decode_fp8",
                           "pa_store_decode_fp8", "pa_prefill_varlen_fp8", "pa_store_prefill",
-                          "pa_store_prefill_fp8"}
+                          "pa_store_prefill_fp8", "pa_store_decode_noalloc"}
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -321,3 +321,32 @@ def test_store_prefill_validation(lib, fp8):
     if fp8:
         assert store_prefill(lib, fp8, kscale=0.0) == SHAPE
         assert store_prefill(lib, fp8, vscale=float("inf")) == SHAPE
+
+
+def test_noalloc_rejects_workspace_beyond_the_array(lib):
+    """pa_store_decode_noalloc refuses, before any HIP call or launch, a call
+    whose split-K workspace exceeds the fixed array (64 MiB), and validates
+    like pa_store_decode otherwise."""
+    import re
+    with open(binding.HEADER) as f:
+        cap = eval(re.search(r"#define PA_NOALLOC_WORKSPACE_BYTES \((.*?)\)", f.read()).group(1).replace("u", ""))
+    assert cap == 64 << 20
+
+    def call(**kw):
+        a = dict(b=512, hq=32, hkv=8, d=128, bs=16, w=2048, n=300000, part=0, dtype=BF16, out=A, slots=A)
+        a.update(kw)
+        return lib.pa_store_decode_noalloc(a["out"], A, a["hq"] * a["d"], A, a["hkv"] * a["d"], A,
+                                           a["hkv"] * a["d"], a["slots"], A, A, A, a["w"], A, a["b"], a["hq"],
+                                           a["hkv"], a["d"], a["bs"], a["n"], 0.088, a["part"], a["dtype"], None)
+    # the 8B-shaped batch at block size 16 needs 272 MiB of partials: refused
+    need = lib.pa_decode_workspace_size(512, 32, 8, 128, 16, 2048, 0)
+    assert need > cap
+    assert call() == WS
+    # half the batch in 4096-token partitions needs 34 MiB: it passes the size
+    # check and fails only on what follows (an unsupported group size here,
+    # so nothing runs)
+    assert lib.pa_decode_workspace_size(256, 32, 8, 128, 16, 2048, 4096) <= cap
+    assert call(b=256, hq=24, part=4096) == UNSUP
+    assert call(out=None, b=4, w=4) == NULL
+    assert call(slots=None, b=4, w=4) == NULL
+    assert call(b=4, w=4, d=96) == UNSUP
