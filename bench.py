@@ -1,33 +1,41 @@
 #!/usr/bin/env python3
 """Benchmark of the paged-attention hot path on one MI355X.
 
-Headline workload (the metric's first half): the Qwen3-0.6B-shaped decode
-step -- 64 sequences, H_q=16, H_kv=8, D=128, bf16, block size 256, a shuffled
-pool of 4096 blocks, context lengths uniform in [128, 4096]. One step is
-pa_store_decode: the scatter of the 64 new tokens and the decode over every
-sequence's whole history in one launch (the same step as two calls,
-pa_store_kvcache then pa_decode, is timed too and reported in components). Inputs are generated on the device (seed 0) before
-timing; an untimed read of a 1 GiB buffer evicts L2/MALL before each step so
-every step reads its KV cold, as a layer's KV would be in a real model step
-(a read, not a write, so no dirty lines are left for the step to write back).
+The metric has two halves, each reported against its roofline:
 
-Also measured in the same run (unless --quick): the chunked varlen prefill
-workload (16384 query tokens over 24 sequences with shared cached prefixes:
-store + pa_prefill_varlen; the metric's second half; the same step as one
-pa_store_prefill launch is timed too), the 8B-shaped
-large-batch decode at block sizes 16 and 256, the 131072-token
-long-context split-K decode, and the headline decode, the long-context
-decode and the chunked prefill again over fp8 (E4M3) caches.
+* decode KV-read GB/s (headline `value`, `roofline`): the 8B-shaped
+  large-batch decode step at block size 16 -- 512 sequences, H_q=32,
+  H_kv=8, D=128, bf16, context lengths log-uniform in [512, 32768], a pool
+  of 1.1x the needed blocks with random placement (the largest decode
+  workload). One step is pa_store_decode: the scatter of the 512 new tokens
+  and the decode over every sequence's whole history in one launch (plus
+  the split-K merge); the same step as two calls (pa_store_kvcache, then
+  pa_decode) is timed too;
+* prefill TFLOP/s (`roofline_prefill`): the chunked varlen prefill -- 16384
+  query tokens over 24 sequences with shared cached prefixes; pa_prefill_varlen
+  after the chunk's pa_store_kvcache, and the same step as one
+  pa_store_prefill launch.
 
-Prints one JSON line. `value` = decode algorithmic bytes per step / step
-time. `roofline` describes the fused call (the dominant kernel) timed with
-HIP events on the stream it runs on. `cpu_baseline` times the fp64 oracle on
-the host over a bounded sample of the same workload.
+Inputs are generated on the device (seed 0) before timing; an untimed read
+of a 1 GiB buffer evicts L2/MALL before each timed call, so every call reads
+its KV cold, as a layer's KV would be in a model step (a read, not a write,
+so no dirty lines are left for the call to write back). Every workload runs
+`--warmup` untimed and `--steps` timed calls of each variant; the JSON
+reports means (value, rooflines), medians and p10/p90.
+
+Also measured (unless --quick): the same decode at block size 256, the
+Qwen3-0.6B-shaped decode, the 131072-token long-context split-K decode, the
+fp8 (E4M3) cache variants, and small-batch decode issued eagerly and as HIP
+graph replays.
+
+Prints one JSON line. `cpu_baseline` / `cpu_baseline_prefill` time the fp64
+oracle on the host over a bounded sample of the decode and prefill
+workloads. `library` is pa_version(), whose source hash must equal this
+tree's (checked before anything runs).
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -40,8 +48,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
 METRIC = "decode KV-read GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak), 1 GPU"
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_66_amd", "csrc", "decode.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "store_decode_traffic.json")
+HEADLINE = "8b-decode-bs16"
+PREFILL = "chunked-prefill"
 
 
 def log(msg):
@@ -54,27 +62,28 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
-    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--quick", action="store_true", help="the two roofline workloads only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget per baseline")
     ap.add_argument("--partition", type=int, default=0, help="decode partition (0 = library default)")
     return ap.parse_args()
 
 
-def kernel_sha(path=DECODE_SRC):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
 
 
-def stored_traffic():
-    """Per-launch HBM bytes of the decode call from committed rocprofv3 --pmc
-    runs, or None when absent or taken on a different kernel source."""
+def stored_traffic(workload, kind):
+    """Per-launch HBM bytes of the workload's timed call from committed
+    rocprofv3 --pmc runs, or None when absent or taken on other kernel
+    sources (the stamp is the SHA-256 of the kernel family's sources)."""
+    from paged_kv_cache_66_amd import srchash
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_sha256") != kernel_sha():
+    if rec.get("kernel_sha256") != srchash.kernel_sha256(kind):
         return None
     return rec.get("bytes_per_launch")
 
@@ -85,10 +94,10 @@ def flush_caches(scratch):
 
 
 class Timer:
-    """Per-step HIP events on the current stream."""
+    """Per-step HIP events on the current stream (the stream the library's
+    calls are enqueued on)."""
 
     def __init__(self, torch, n, marks):
-        self.torch = torch
         self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(marks)] for _ in range(n)]
 
     def rec(self, step, mark):
@@ -98,7 +107,25 @@ class Timer:
         return [e[a].elapsed_time(e[b]) for e in self.ev]
 
 
-def run_decode(torch, binding, wl, w, steps, warmup, flush, scratch, partition=0, label=None):
+def summary(ms):
+    """mean, median, p10, p90 of a list of per-call times (ms)."""
+    s = sorted(ms)
+    n = len(s)
+    return dict(mean=sum(s) / n, median=s[n // 2], p10=s[n // 10], p90=s[min(n - 1, (9 * n) // 10)])
+
+
+def rounded(d, nd=5):
+    if isinstance(d, dict):
+        return {k: rounded(v, nd) for k, v in d.items()}
+    if isinstance(d, list):
+        return [rounded(v, nd) for v in d]
+    return round(d, nd) if isinstance(d, float) else d
+
+
+def run_decode(torch, binding, wl, w, steps, warmup, flush, scratch, partition=0):
+    """Time one decode workload: the step as two calls (store, then decode;
+    events around each) and as one fused call, `warmup` untimed and `steps`
+    timed calls of each, the caches evicted before every timed call."""
     t = wl.make_device_tensors(w)
     slots = torch.from_numpy(w.slot_mapping).cuda()
     tables = torch.from_numpy(w.block_tables).cuda()
@@ -107,10 +134,9 @@ def run_decode(torch, binding, wl, w, steps, warmup, flush, scratch, partition=0
     need = binding.pa_decode_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                             w.block_size, w.max_blocks_per_seq, partition)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
-
     fp8 = w.cache_dtype == "fp8e4m3"
 
-    def step():
+    def store():
         if fp8:
             binding.pa_store_kvcache_fp8(t["k"], t["v"], t["k_cache"], t["v_cache"], slots, w.k_scale,
                                          w.v_scale)
@@ -134,28 +160,23 @@ def run_decode(torch, binding, wl, w, steps, warmup, flush, scratch, partition=0
             binding.pa_store_decode(t["q"], t["k"], t["v"], slots, t["k_cache"], t["v_cache"], tables, ctx,
                                     w.scale, out=out, workspace=ws, partition_size=partition)
 
-    for _ in range(warmup):
-        step()
-        dec()
+    for _ in range(warmup):  # cold like the timed calls, so every call of a kernel sees the same state
+        for fn in (store, dec, fused):
+            if flush:
+                flush_caches(scratch)
+            fn()
     torch.cuda.synchronize()
     timer = Timer(torch, steps, 3)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for s in range(steps):
         if flush:
             flush_caches(scratch)
         timer.rec(s, 0)
-        step()
+        store()
         timer.rec(s, 1)
         dec()
         timer.rec(s, 2)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = timer.span(0, 2)
-    dec_ms = timer.span(1, 2)
-    store_ms = timer.span(0, 1)
     assert bool(torch.isfinite(out.float()).all()), f"{w.name}: non-finite decode output"
-    # the same step as one launch (pa_store_decode)
     ftimer = Timer(torch, steps, 2)
     for s in range(steps):
         if flush:
@@ -164,30 +185,33 @@ def run_decode(torch, binding, wl, w, steps, warmup, flush, scratch, partition=0
         fused()
         ftimer.rec(s, 1)
     torch.cuda.synchronize()
-    fused_list = ftimer.span(0, 1)
-    fused_ms = sum(fused_list) / steps
+    assert bool(torch.isfinite(out.float()).all()), f"{w.name}: non-finite fused output"
     res = dict(
-        workload=label or w.name,
-        step_ms=sum(step_ms) / steps,
-        decode_ms=sum(dec_ms) / steps,
-        decode_ms_p10_p90=[sorted(dec_ms)[steps // 10], sorted(dec_ms)[(9 * steps) // 10]],
-        store_us=1000 * sum(store_ms) / steps,
-        fused_step_ms=fused_ms,
-        fused_ms_median=sorted(fused_list)[steps // 2],
-        fused_ms_p10_p90=[sorted(fused_list)[steps // 10], sorted(fused_list)[(9 * steps) // 10]],
+        workload=w.name,
+        steps=steps,
+        fused_ms=summary(ftimer.span(0, 1)),
+        two_call_ms=summary(timer.span(0, 2)),
+        decode_ms=summary(timer.span(1, 2)),
+        store_ms=summary(timer.span(0, 1)),
         bytes_logical=w.algorithmic_bytes(unique=False),
         bytes_unique=w.algorithmic_bytes(unique=True),
         flops=w.flops(),
-        wall_s=wall,
     )
-    res["decode_GBps"] = res["bytes_logical"] / (res["decode_ms"] * 1e-3) / 1e9
-    res["decode_GBps_unique"] = res["bytes_unique"] / (res["decode_ms"] * 1e-3) / 1e9
-    res["hbm_frac"] = res["decode_GBps_unique"] / HBM_PEAK_GBS
+    # the fused call also writes the new rows and reads the slot mapping
+    res["fused_bytes"] = res["bytes_logical"] + w.num_seqs * 2 * w.num_kv_heads * w.head_dim * \
+        (1 if fp8 else w.elem_bytes) + 4 * w.num_seqs
+    for key in ("fused_ms", "decode_ms"):
+        m = res[key]["mean"] * 1e-3
+        res[key.replace("_ms", "_GBps")] = res["bytes_logical"] / m / 1e9
+        res[key.replace("_ms", "_GBps_unique")] = res["bytes_unique"] / m / 1e9
+    res["hbm_frac_unique"] = res["fused_GBps_unique"] / HBM_PEAK_GBS
     del t
-    return res, out
+    return res
 
 
 def run_prefill(torch, binding, wl, w, steps, warmup, flush, scratch):
+    """Time the prefill step: the chunk's scatter then pa_prefill_varlen
+    (events around each), and the same step as one fused call."""
     t = wl.make_device_tensors(w)
     slots = torch.from_numpy(w.slot_mapping).cuda()
     cuq = torch.from_numpy(w.cu_seqlens_q).cuda()
@@ -221,9 +245,10 @@ def run_prefill(torch, binding, wl, w, steps, warmup, flush, scratch):
                                      w.max_seqlen_q, w.max_seqlen_k, tables, w.scale, out=out)
 
     for _ in range(warmup):
-        store()
-        pre()
-        fused()
+        for fn in (store, pre, fused):
+            if flush:
+                flush_caches(scratch)
+            fn()
     torch.cuda.synchronize()
     timer = Timer(torch, steps, 3)
     for s in range(steps):
@@ -236,11 +261,6 @@ def run_prefill(torch, binding, wl, w, steps, warmup, flush, scratch):
         timer.rec(s, 2)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(out.float()).all()), "prefill: non-finite output"
-    pre_list = timer.span(1, 2)
-    pre_ms = sum(pre_list) / steps
-    store_ms = sum(timer.span(0, 1)) / steps
-    step_ms = sum(timer.span(0, 2)) / steps
-    # the same step as one launch (pa_store_prefill)
     ftimer = Timer(torch, steps, 2)
     for s in range(steps):
         if flush:
@@ -249,21 +269,22 @@ def run_prefill(torch, binding, wl, w, steps, warmup, flush, scratch):
         fused()
         ftimer.rec(s, 1)
     torch.cuda.synchronize()
-    fused_ms = sum(ftimer.span(0, 1)) / steps
     flops = w.flops()
     res = dict(
         workload=w.name,
-        prefill_ms=pre_ms,
-        prefill_ms_median=sorted(pre_list)[steps // 2],
-        prefill_ms_p10_p90=[sorted(pre_list)[steps // 10], sorted(pre_list)[(9 * steps) // 10]],
+        steps=steps,
+        prefill_ms=summary(timer.span(1, 2)),
+        store_ms=summary(timer.span(0, 1)),
+        two_call_ms=summary(timer.span(0, 2)),
+        fused_ms=summary(ftimer.span(0, 1)),
         flops=flops,
-        prefill_TFLOPs=flops / (pre_ms * 1e-3) / 1e12,
-        store_us=1000 * store_ms,
-        store_GBps=w.store_bytes() / (store_ms * 1e-3) / 1e9,
-        step_ms=step_ms,
-        fused_step_ms=fused_ms,
+        store_bytes=w.store_bytes(),
     )
+    res["prefill_TFLOPs"] = flops / (res["prefill_ms"]["mean"] * 1e-3) / 1e12
+    res["prefill_TFLOPs_median"] = flops / (res["prefill_ms"]["median"] * 1e-3) / 1e12
+    res["fused_TFLOPs"] = flops / (res["fused_ms"]["mean"] * 1e-3) / 1e12
     res["mfma_frac"] = res["prefill_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
+    res["store_GBps"] = w.store_bytes() / (res["store_ms"]["mean"] * 1e-3) / 1e9
     del t
     return res
 
@@ -332,11 +353,46 @@ def run_graph_small(torch, binding, wl, steps=100):
     return res
 
 
-def cpu_baseline(torch, wl, w, seconds):
-    """fp64 oracle on the host over the decode workload: host copies of every
-    sequence's blocks are taken first (untimed), then the oracle's store +
-    decode runs sequence by sequence, in passes over the batch, until the
-    time budget is spent. Only the oracle's compute is timed."""
+def host_info():
+    """Host cores and the BLAS NumPy uses (vendor, threads)."""
+    import numpy as np
+    info = {"cpu_count": os.cpu_count()}
+    try:
+        info["affinity"] = len(os.sched_getaffinity(0))
+    except AttributeError:
+        pass
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        info["blas"] = f"{blas.get('name')} {blas.get('version', '')}".strip()
+    except Exception:  # noqa: BLE001 - older numpy: no dict mode
+        info["blas"] = None
+    try:
+        from threadpoolctl import threadpool_info
+        pools = threadpool_info()
+        info["blas_threads"] = max((p.get("num_threads", 1) for p in pools), default=1)
+        info["threadpools"] = [f"{p.get('internal_api')}:{p.get('num_threads')}" for p in pools]
+    except Exception:  # noqa: BLE001
+        info["blas_threads"] = None
+    return info
+
+
+def one_thread():
+    """Context that holds NumPy's BLAS to one thread, so the oracle's
+    timing uses exactly one core (a no-op context without threadpoolctl,
+    which the host report then shows)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=1)
+    except Exception:  # noqa: BLE001
+        import contextlib
+        return contextlib.nullcontext()
+
+
+def cpu_baseline_decode(torch, wl, w, seconds):
+    """fp64 oracle on the host over the decode workload, sequence by
+    sequence in order: each sequence's blocks are copied to the host
+    (untimed), then the oracle's store of the new row and its decode run
+    (timed), until the time budget is spent. One thread runs the oracle."""
     import numpy as np
 
     import oracle
@@ -344,45 +400,103 @@ def cpu_baseline(torch, wl, w, seconds):
 
     t = wl.make_device_tensors(w)
     bs = w.block_size
-    host = []
+    q_h, k_h, v_h = (to_host(t[x], w.dtype) for x in ("q", "k", "v"))
+    done_bytes, done, spent = 0, 0, 0.0
     for b in range(w.num_seqs):
         n = int(w.context_lens[b])
         nb = wl.num_blocks_for(n, bs)
         ids = torch.from_numpy(w.block_tables[b, :nb].astype(np.int64)).cuda()
-        host.append(dict(n=n, nb=nb, k=to_host(t["k_cache"].index_select(0, ids), w.dtype),
-                         v=to_host(t["v_cache"].index_select(0, ids), w.dtype),
-                         q=to_host(t["q"][b:b + 1], w.dtype), nk=to_host(t["k"][b:b + 1], w.dtype),
-                         nv=to_host(t["v"][b:b + 1], w.dtype)))
-    del t
-    done_bytes, done, spent = 0, 0, 0.0
-    while spent < seconds:
-        for h in host:
-            kh, vh = h["k"].copy(), h["v"].copy()
-            n, nb = h["n"], h["nb"]
+        kh = to_host(t["k_cache"].index_select(0, ids), w.dtype)
+        vh = to_host(t["v_cache"].index_select(0, ids), w.dtype)
+        with one_thread():
             c0 = time.perf_counter()
-            oracle.store_kvcache(h["nk"], h["nv"], kh, vh, np.array([(nb - 1) * bs + (n - 1) % bs], np.int32))
-            oracle.decode(h["q"], kh, vh, np.arange(nb, dtype=np.int32)[None], np.array([n], np.int32),
+            oracle.store_kvcache(k_h[b:b + 1], v_h[b:b + 1], kh, vh,
+                                 np.array([(nb - 1) * bs + (n - 1) % bs], np.int32))
+            oracle.decode(q_h[b:b + 1], kh, vh, np.arange(nb, dtype=np.int32)[None], np.array([n], np.int32),
                           w.scale, w.dtype)
             spent += time.perf_counter() - c0
-            done += 1
-            done_bytes += n * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes + \
-                2 * w.num_q_heads * w.head_dim * w.elem_bytes + nb * 4 + 4
-            if spent >= seconds:
-                break
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:
-        threads = None
+        done += 1
+        done_bytes += n * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes + \
+            2 * w.num_q_heads * w.head_dim * w.elem_bytes + nb * 4 + 4
+        if spent >= seconds:
+            break
+    del t
+    info = host_info()
     return {
         "value": round(done_bytes / spent / 1e9, 4),
         "unit": "GB/s",
-        "cores": threads or 1,
+        "cores": 1,
         "kind": "oracle",
-        "sample": f"{done} sequence decodes ({done / w.num_seqs:.1f} passes over the {w.num_seqs} "
-                  f"sequences of {w.name}; fp64 NumPy store + decode), {spent:.1f} s of oracle "
-                  f"compute; host has {os.cpu_count()} CPUs, BLAS threads as in cores",
+        "sample": f"the first {done} of the {w.num_seqs} sequences of {w.name} ({done_bytes / 1e9:.2f} GB of "
+                  f"the step's {w.algorithmic_bytes() / 1e9:.2f} GB; fp64 NumPy store + decode, one sequence "
+                  f"at a time on one thread), {spent:.1f} s of oracle compute",
+        "host": info,
+    }
+
+
+def cpu_baseline_prefill(torch, wl, w, seconds):
+    """fp64 oracle on the host over the prefill workload: the caches, queries
+    and new rows are copied to the host and the oracle stores the chunk
+    (untimed); then rows are computed sequence by sequence, a seeded sample
+    of rows per sequence, until the time budget is spent. The flop count is
+    the metric's (QK^T + PV over the unmasked pairs) for the rows done."""
+    import numpy as np
+
+    import oracle
+    from tests.helpers import to_host
+
+    t = wl.make_device_tensors(w)
+    kc, vc = to_host(t["k_cache"], w.dtype), to_host(t["v_cache"], w.dtype)
+    q_h, k_h, v_h = (to_host(t[x], w.dtype) for x in ("q", "k", "v"))
+    del t
+    oracle.store_kvcache(k_h, v_h, kc, vc, w.slot_mapping)
+    rng = np.random.default_rng(7)
+    done_rows, flops, spent = 0, 0.0, 0.0
+    while spent < seconds:
+        for i in range(w.num_seqs):
+            q0, q1 = int(w.cu_seqlens_q[i]), int(w.cu_seqlens_q[i + 1])
+            lq, lk = q1 - q0, int(w.cu_seqlens_k[i + 1] - w.cu_seqlens_k[i])
+            if lq == 0:
+                continue
+            rows = sorted(set(int(x) for x in rng.integers(0, lq, 4)))
+            with one_thread():
+                c0 = time.perf_counter()
+                oracle.prefill_varlen(q_h[q0:q1], kc, vc, np.array([0, lq], np.int32),
+                                      np.array([0, lk], np.int32), w.block_tables[i:i + 1], w.scale, w.dtype,
+                                      rows=rows)
+                spent += time.perf_counter() - c0
+            done_rows += len(rows)
+            flops += sum(4.0 * w.head_dim * w.num_q_heads * (lk - lq + j + 1) for j in rows)
+            if spent >= seconds:
+                break
+    return {
+        "value": round(flops / spent / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done_rows} query rows of {w.name} (4 seeded rows per sequence per pass, all 32 heads; "
+                  f"{flops / 1e9:.1f} GFLOP of the step's {w.flops() / 1e12:.3f} TFLOP; fp64 NumPy, one "
+                  f"thread), {spent:.1f} s of oracle compute",
+        "host": host_info(),
+    }
+
+
+def decode_roofline(res, traffic):
+    fm = res["fused_ms"]["mean"]
+    achieved = res["fused_bytes"] / (fm * 1e-3) / 1e9
+    return {
+        "bound": "hbm",
+        "achieved": round(achieved, 2),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "workload": res["workload"],
+        "kernel": "pa_store_decode (decode_partition_kernel<BF16Tag, 128, G, true> + decode_reduce_kernel)",
+        "algorithmic_bytes_per_launch": res["fused_bytes"],
+        "avg_launch_ms": round(fm, 5),
+        "median_launch_ms": round(res["fused_ms"]["median"], 5),
+        "p10_p90_launch_ms": [round(res["fused_ms"]["p10"], 5), round(res["fused_ms"]["p90"], 5)],
     }
 
 
@@ -398,70 +512,68 @@ def main():
     from paged_kv_cache_66_amd import workloads as wl
 
     binding.load()
+    binding.check_source_hash()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     flush = not args.no_flush
     scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda") if flush else None
+    steps, warm = args.steps, args.warmup
 
-    w = wl.qwen3_0p6b_decode(0)
-    log(f"[bench] {w.name}: warmup {args.warmup}, steps {args.steps}")
-    head, _ = run_decode(torch, binding, wl, w, args.steps, args.warmup, flush, scratch, args.partition)
-    log(f"[bench] {w.name}: decode {head['decode_ms'] * 1e3:.1f} us, {head['decode_GBps']:.0f} GB/s")
+    w = wl.DECODE_CONFIGS[HEADLINE](0)
+    log(f"[bench] {w.name}: warmup {warm}, steps {steps}")
+    head = run_decode(torch, binding, wl, w, steps, warm, flush, scratch, args.partition)
+    torch.cuda.empty_cache()
+    log(f"[bench] {w.name}: fused {head['fused_ms']['mean'] * 1e3:.1f} us, {head['fused_GBps']:.0f} GB/s")
+
+    wp = wl.PREFILL_CONFIGS[PREFILL](0)
+    log(f"[bench] {wp.name}")
+    pre = run_prefill(torch, binding, wl, wp, steps, warm, flush, scratch)
+    torch.cuda.empty_cache()
+    log(f"[bench] {wp.name}: prefill {pre['prefill_ms']['mean']:.3f} ms, {pre['prefill_TFLOPs']:.1f} TFLOP/s")
 
     secondary = {}
     if not args.quick:
-        ks = max(5, args.steps // 3)
-        for name, mk in [("8b-decode-bs16", lambda: wl.large_batch_decode(16, 0)),
-                         ("8b-decode-bs256", lambda: wl.large_batch_decode(256, 0)),
-                         ("long-context-decode", lambda: wl.long_context_decode(0)),
-                         ("qwen3-0.6b-decode-fp8", lambda: wl.DECODE_CONFIGS["qwen3-0.6b-decode-fp8"](0)),
-                         ("long-context-decode-fp8", lambda: wl.DECODE_CONFIGS["long-context-decode-fp8"](0))]:
+        for name in ("8b-decode-bs256", "qwen3-0.6b-decode", "long-context-decode", "qwen3-0.6b-decode-fp8",
+                     "long-context-decode-fp8"):
             log(f"[bench] {name}")
-            r, _ = run_decode(torch, binding, wl, mk(), ks, 2, flush, scratch, args.partition, name)
+            r = run_decode(torch, binding, wl, wl.DECODE_CONFIGS[name](0), steps, warm, flush, scratch,
+                           args.partition)
             torch.cuda.empty_cache()
-            secondary[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
-            log(f"[bench] {name}: decode {r['decode_ms']:.3f} ms, {r['decode_GBps_unique']:.0f} GB/s unique")
+            if name in ("8b-decode-bs256", "qwen3-0.6b-decode"):
+                r["roofline"] = decode_roofline(r, stored_traffic(name, "decode"))
+            secondary[name] = rounded(r, 4)
+            log(f"[bench] {name}: fused {r['fused_ms']['mean']:.4f} ms, {r['fused_GBps_unique']:.0f} GB/s unique")
         log("[bench] graph replay, small batch")
         secondary["decode-graph-small"] = run_graph_small(torch, binding, wl)
         log(f"[bench] small batch: {secondary['decode-graph-small']}")
-        log("[bench] chunked-prefill")
-        p = run_prefill(torch, binding, wl, wl.chunked_prefill(0), ks, 2, flush, scratch)
+        name = "chunked-prefill-fp8"
+        log(f"[bench] {name}")
+        p = run_prefill(torch, binding, wl, wl.PREFILL_CONFIGS[name](0), steps, warm, flush, scratch)
         torch.cuda.empty_cache()
-        secondary["chunked-prefill"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in p.items()}
-        log(f"[bench] prefill {p['prefill_ms']:.3f} ms, {p['prefill_TFLOPs']:.1f} TFLOP/s; "
-            f"store+prefill {p['step_ms']:.3f} ms, fused {p['fused_step_ms']:.3f} ms")
-        log("[bench] chunked-prefill-fp8")
-        p = run_prefill(torch, binding, wl, wl.PREFILL_CONFIGS["chunked-prefill-fp8"](0), ks, 2, flush, scratch)
-        torch.cuda.empty_cache()
-        secondary["chunked-prefill-fp8"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in p.items()}
-        log(f"[bench] prefill fp8 {p['prefill_ms']:.3f} ms, {p['prefill_TFLOPs']:.1f} TFLOP/s; "
-            f"store+prefill {p['step_ms']:.3f} ms, fused {p['fused_step_ms']:.3f} ms")
+        secondary[name] = rounded(p, 4)
+        log(f"[bench] {name}: prefill {p['prefill_ms']['mean']:.3f} ms, {p['prefill_TFLOPs']:.1f} TFLOP/s")
 
-    cpu = None
+    cpu = cpu_pre = None
     if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle)")
-        cpu = cpu_baseline(torch, wl, w, args.cpu_seconds)
+        log("[bench] cpu baseline (oracle), decode")
+        cpu = cpu_baseline_decode(torch, wl, w, args.cpu_seconds)
+        log("[bench] cpu baseline (oracle), prefill")
+        cpu_pre = cpu_baseline_prefill(torch, wl, wp, args.cpu_seconds)
 
-    # The step is the fused call: the scatter of the 64 new rows and the
-    # decode in one launch (plus the merge). Its algorithmic bytes are the
-    # decode's (the new rows are read once, from the inputs) plus the rows it
-    # writes into the caches and the slot mapping.
-    step_bytes = head["bytes_logical"] + w.num_seqs * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes + 4 * w.num_seqs
-    achieved = step_bytes / (head["fused_step_ms"] * 1e-3) / 1e9
-    value = head["bytes_logical"] / (head["fused_step_ms"] * 1e-3) / 1e9
+    pm = pre["prefill_ms"]["mean"]
     rec = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(head["fused_GBps"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(head["fused_step_ms"], 5),
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(head["fused_ms"]["mean"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) K/V/q on the device; shuffled block pool)",
+        "data": "synthetic (seeded N(0,1) K/V/q generated on the device; random block placement)",
         "config": {
             "workload": w.name,
             "batch": w.num_seqs,
@@ -470,34 +582,36 @@ def main():
             "head_dim": w.head_dim,
             "block_size": w.block_size,
             "num_blocks": w.num_blocks,
-            "context_lens": "uniform[128,4096], seed 0",
+            "context_lens": "round(exp(U(ln 512, ln 32768))), seed 0",
             "sum_context": int(w.context_lens.sum()),
-            "step": "pa_store_decode: scatter of the 64 new K/V rows + decode, one launch (+ split-K merge)",
-            "cache": "cold (L2/MALL evicted before each step)" if flush else "warm",
+            "step": "pa_store_decode: scatter of the 512 new K/V rows + decode, one launch (+ split-K merge)",
+            "value_is": "decode algorithmic bytes / mean fused-call time",
+            "cache": "cold (L2/MALL evicted before each call)" if flush else "warm",
             "parallelism": "none (1 GPU)",
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": stored_traffic(),
-            "kernel": "pa_store_decode (decode_partition_kernel<..., FUSED> + decode_reduce_kernel)",
-            "algorithmic_bytes_per_launch": step_bytes,
-            "avg_launch_ms": round(head["fused_step_ms"], 5),
+        "roofline": decode_roofline(head, stored_traffic(HEADLINE, "decode")),
+        "roofline_prefill": {
+            "bound": "mfma",
+            "achieved": round(pre["prefill_TFLOPs"], 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(pre["prefill_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": stored_traffic(PREFILL, "prefill"),
+            "workload": wp.name,
+            "kernel": "pa_prefill_varlen (prefill_direct_kernel<128, 4, false>)",
+            "algorithmic_flops_per_launch": pre["flops"],
+            "avg_launch_ms": round(pm, 5),
+            "median_launch_ms": round(pre["prefill_ms"]["median"], 5),
+            "p10_p90_launch_ms": [round(pre["prefill_ms"]["p10"], 5), round(pre["prefill_ms"]["p90"], 5)],
         },
         "cpu_baseline": cpu,
+        "cpu_baseline_prefill": cpu_pre,
         "components": {
-            "fused_step_ms_median": round(head["fused_ms_median"], 5),
-            "fused_step_ms_p10_p90": [round(x, 5) for x in head["fused_ms_p10_p90"]],
-            "two_call_step_ms": round(head["step_ms"], 5),
-            "decode_ms": round(head["decode_ms"], 5),
-            "decode_ms_p10_p90": [round(x, 5) for x in head["decode_ms_p10_p90"]],
-            "decode_GBps": round(head["bytes_logical"] / (head["decode_ms"] * 1e-3) / 1e9, 2),
-            "store_us": round(head["store_us"], 2),
+            "decode": rounded(head, 5),
+            "prefill": rounded(pre, 5),
         },
         "secondary": secondary,
+        "library": binding.version(),
     }
     print(json.dumps(rec), flush=True)
 
