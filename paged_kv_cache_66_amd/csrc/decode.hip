@@ -84,6 +84,31 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// A row's G scores go to LDS as whole 16-byte (or 8 / 4-byte) stores: the
+// row's slot s_score[t * G .. + G) is aligned to its own size.
+template <int G>
+__device__ __forceinline__ void store_scores(float* dst, const float (&sc)[G]) {
+  if constexpr (G % 4 == 0) {
+#pragma unroll
+    for (int h = 0; h < G; h += 4)
+      *reinterpret_cast<float4*>(dst + h) = make_float4(sc[h], sc[h + 1], sc[h + 2], sc[h + 3]);
+  } else if constexpr (G == 2) {
+    *reinterpret_cast<float2*>(dst) = make_float2(sc[0], sc[1]);
+  } else {
+    dst[0] = sc[0];
+  }
+}
+
+// v + the same register of lane l ^ 16, then of lane l ^ 32: the cross-row
+// swaps v_permlane16_swap / v_permlane32_swap return a value and its
+// partner's (in either order), so every lane of the four gets the same sum.
+__device__ __forceinline__ float sum_lanes_16_32(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Query slice of one head held by a lane for the score pass: two 16-byte
 // vectors of the head's row, in the form the dot product wants: fp32 values
 // for fp32 caches, raw bf16 pairs for bf16 caches (products of two bf16
@@ -226,7 +251,8 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   float* s_score = lds + kNewWords;                       // [partition][G]
   float* s_max = s_score + score_words;                   // [G]
   float* s_sum = s_max + G;                               // [G]
-  int32_t* s_ids = reinterpret_cast<int32_t*>(s_sum + G);  // block ids of the partition
+  float* s_wred = s_sum + G;                              // [kWaves][G] per-wave maxima, then sums
+  int32_t* s_ids = reinterpret_cast<int32_t*>(s_wred + kWaves * G);  // block ids of the partition
 
   // Dispatch order: kv head fastest, then sequence, then partition. The
   // workgroups that read the head slices of the same token rows run side by
@@ -363,10 +389,7 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
       float sc[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) sc[h] = group_sum<LPT1>(qs[h].dot(k0[u], k1[u]));
-      if (li1 == 0 && tl < nloop) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) s_score[tl * G + h] = sc[h];
-      }
+      if (li1 == 0 && tl < nloop) store_scores<G>(s_score + tl * G, sc);
     }
   }
   if constexpr (FUSED) {
@@ -376,34 +399,71 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
       float sc[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) sc[h] = group_sum<LPT1>(qs[h].dot(nk0, nk1));
-      if (li1 == 0 && my_row1 == new_tl % STEP1) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) s_score[new_tl * G + h] = sc[h];
-      }
+      if (li1 == 0 && my_row1 == new_tl % STEP1) store_scores<G>(s_score + new_tl * G, sc);
     }
   }
   __syncthreads();
 
   // phase 2: exact max and sum of exp2(s - max) per head, in the log2 domain
   // (s = raw score * scale * log2 e; scale > 0 so the raw max is the max);
-  // p overwrites the raw score
-  for (int h = wave; h < G; h += kWaves) {
-    float m = -INFINITY;
-    for (int t = lane; t < ntok; t += 64) m = fmaxf(m, s_score[t * G + h]);
-    m = wave_max(m) * scale_log2;
-    float l = 0.f;
-    for (int t = lane; t < ntok; t += 64) {
-      const float e = exp2f(fmaf(s_score[t * G + h], scale_log2, -m));
-      s_score[t * G + h] = e;
-      l += e;
+  // p overwrites the raw score. Thread tid owns head tid % G and every
+  // (256 / G)-th token of it, so its loads are independent and several are
+  // in flight at once; the per-head maxima and sums combine the threads of a
+  // head (lanes of a wave with the same head differ in the lane bits at and
+  // above G, then the waves through LDS).
+  constexpr int kTph = kThreads / G;  // threads per head
+  const int hh = tid % G;
+  {
+    float mt = -INFINITY;
+    int t = tid / G;
+    for (; t + 3 * kTph < ntok; t += 4 * kTph) {
+      float e[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) e[j] = s_score[(t + j * kTph) * G + hh];
+      mt = fmaxf(mt, fmaxf(fmaxf(e[0], e[1]), fmaxf(e[2], e[3])));
     }
-    l = wave_sum(l);
-    if (lane == 0) {
-      s_max[h] = m;
-      s_sum[h] = l;
-    }
+    for (; t < ntok; t += kTph) mt = fmaxf(mt, s_score[t * G + hh]);
+#pragma unroll
+    for (int off = G; off < 64; off <<= 1) mt = fmaxf(mt, __shfl_xor(mt, off, 64));
+    if (lane < G) s_wred[wave * G + lane] = mt;
   }
   __syncthreads();
+  float m = s_wred[hh];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_wred[w * G + hh]);
+  m *= scale_log2;
+  float l = 0.f;
+  {
+    int t = tid / G;
+    for (; t + 3 * kTph < ntok; t += 4 * kTph) {
+      float e[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) e[j] = s_score[(t + j * kTph) * G + hh];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        e[j] = exp2f(fmaf(e[j], scale_log2, -m));
+        s_score[(t + j * kTph) * G + hh] = e[j];
+        l += e[j];
+      }
+    }
+    for (; t < ntok; t += kTph) {
+      const float e = exp2f(fmaf(s_score[t * G + hh], scale_log2, -m));
+      s_score[t * G + hh] = e;
+      l += e;
+    }
+  }
+#pragma unroll
+  for (int off = G; off < 64; off <<= 1) l += __shfl_xor(l, off, 64);
+  __syncthreads();  // every wave has read the maxima: s_wred becomes the sums
+  if (lane < G) s_wred[wave * G + lane] = l;
+  if (tid < G) s_max[tid] = m;
+  __syncthreads();
+  if (tid < G) {
+    float sum = s_wred[tid];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) sum += s_wred[w * G + tid];
+    s_sum[tid] = sum;
+  }
 
   // phase 3: weighted sum of V rows
   float acc[G][EPV];
@@ -458,8 +518,12 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
       float v = acc[h][e];
+      if constexpr (LPT == 16) {
+        v = sum_lanes_16_32(v);  // the rows of a wave: lanes l, l ^ 16, l ^ 32, l ^ 48
+      } else {
 #pragma unroll
-      for (int off = LPT; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+        for (int off = LPT; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+      }
       acc[h][e] = v;
     }
   __syncthreads();  // all reads of p are done; the score area becomes the reduction area
@@ -568,7 +632,7 @@ hipError_t launch_decode_typed(const DecodeArgs& a, hipStream_t stream) {
   const int score_words = G * (a.partition > 4 * D ? a.partition : 4 * D);
   const int max_ids = a.partition / (a.block_size < a.partition ? a.block_size : a.partition) + 2;
   const int new_words = FUSED ? 2 * D * Elem<T>::kBytes / 4 : 0;  // the fused new row
-  const size_t lds = static_cast<size_t>(new_words + score_words + 2 * G + max_ids) * 4;
+  const size_t lds = static_cast<size_t>(new_words + score_words + (2 + kWaves) * G + max_ids) * 4;
   // an E4M3 cache holds K / k_scale: the score scale absorbs k_scale
   const float scale_log2 = a.scale * (Elem<T>::kBytes == 1 ? a.k_scale : 1.f) * kLog2e;
   const int64_t table_rows = static_cast<int64_t>(a.max_blocks) << log2_bs;
