@@ -360,36 +360,84 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 
   const int nloop = new_tl >= 0 ? ntok - 1 : ntok;  // rows read from the cache
 
-  // phase 1: raw scores q . k (the scale is applied once per score in phase 2)
+  // phase 1: raw scores q . k (the scale is applied once per score in phase 2).
+  // Each trip's rows are taken in two halves with their loads in flight while
+  // the other half is scored (software pipelining in the same registers): the
+  // loads of the trip's second half are issued before its first half is
+  // scored, and those of the next trip's first half before the second half
+  // is. Rows past the partition load the partition's last cached row (every
+  // load is unconditional, so the wait counts stay exact) and are not stored.
   const char* kbase1 = k_cache + static_cast<int64_t>(g) * D * EB + li1 * kFirst;
   const int my_row1 = wave * TPW1 + grp1;
-  for (int base = 0; base < nloop; base += STEP1 * kUnroll) {
-    Vec k0[kUnroll], k1[kUnroll];
+  // (An E4M3 cache at G >= 8 keeps the single-buffer form below: the two
+  // halves' extra registers would cost it a wave per SIMD.)
+  constexpr bool kPipe = !(kFp8 && G >= 8);
+  if (kPipe && nloop > 0) {
+    constexpr int H1 = kUnroll / 2;
+    constexpr int TRIP1 = STEP1 * kUnroll;
+    Vec ka[2][H1], kb[2][H1];
+    auto load_k = [&](int base, int half) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int tl = base + u * STEP1 + my_row1;
-      if (tl < nloop) {
+      for (int u = 0; u < H1; ++u) {
+        const int tl = min(base + (half * H1 + u) * STEP1 + my_row1, nloop - 1);
         const char* r = kbase1 + row_off(tl);
         if constexpr (kPair) {
           const Vec16 both = load16_nt(r);
-          k0[u] = Vec{{both.w[0], both.w[1]}};
-          k1[u] = Vec{{both.w[2], both.w[3]}};
+          ka[half][u] = Vec{{both.w[0], both.w[1]}};
+          kb[half][u] = Vec{{both.w[2], both.w[3]}};
         } else {
-          k0[u] = E::load_nt(r);
-          k1[u] = E::load_nt(r + kSecond);
+          ka[half][u] = E::load_nt(r);
+          kb[half][u] = E::load_nt(r + kSecond);
         }
-      } else {
-        k0[u] = Vec{};
-        k1[u] = Vec{};
       }
+    };
+    auto score_k = [&](int base, int half) {
+#pragma unroll
+      for (int u = 0; u < H1; ++u) {
+        const int tl = base + (half * H1 + u) * STEP1 + my_row1;
+        float sc[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) sc[h] = group_sum<LPT1>(qs[h].dot(ka[half][u], kb[half][u]));
+        if (li1 == 0 && tl < nloop) store_scores<G>(s_score + tl * G, sc);
+      }
+    };
+    load_k(0, 0);
+    for (int base = 0; base < nloop; base += TRIP1) {
+      load_k(base, 1);
+      score_k(base, 0);
+      if (base + TRIP1 < nloop) load_k(base + TRIP1, 0);
+      score_k(base, 1);
     }
+  }
+  if constexpr (!kPipe) {
+    for (int base = 0; base < nloop; base += STEP1 * kUnroll) {
+      Vec k0[kUnroll], k1[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int tl = base + u * STEP1 + my_row1;
-      float sc[G];
+      for (int u = 0; u < kUnroll; ++u) {
+        const int tl = base + u * STEP1 + my_row1;
+        if (tl < nloop) {
+          const char* r = kbase1 + row_off(tl);
+          if constexpr (kPair) {
+            const Vec16 both = load16_nt(r);
+            k0[u] = Vec{{both.w[0], both.w[1]}};
+            k1[u] = Vec{{both.w[2], both.w[3]}};
+          } else {
+            k0[u] = E::load_nt(r);
+            k1[u] = E::load_nt(r + kSecond);
+          }
+        } else {
+          k0[u] = Vec{};
+          k1[u] = Vec{};
+        }
+      }
 #pragma unroll
-      for (int h = 0; h < G; ++h) sc[h] = group_sum<LPT1>(qs[h].dot(k0[u], k1[u]));
-      if (li1 == 0 && tl < nloop) store_scores<G>(s_score + tl * G, sc);
+      for (int u = 0; u < kUnroll; ++u) {
+        const int tl = base + u * STEP1 + my_row1;
+        float sc[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) sc[h] = group_sum<LPT1>(qs[h].dot(k0[u], k1[u]));
+        if (li1 == 0 && tl < nloop) store_scores<G>(s_score + tl * G, sc);
+      }
     }
   }
   if constexpr (FUSED) {
@@ -472,28 +520,63 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 #pragma unroll
     for (int e = 0; e < EPV; ++e) acc[h][e] = 0.f;
 
-  for (int base = 0; base < nloop; base += STEP * kUnrollV) {
-    Vec vv[kUnrollV];
+  // the same two-half pipelining as the score pass; every lane still adds
+  // its rows in increasing order
+  if (kPipe && nloop > 0) {
+    constexpr int HV = kUnrollV / 2;
+    constexpr int TRIPV = STEP * kUnrollV;
+    Vec vv[2][HV];
+    auto load_v = [&](int base, int half) {
 #pragma unroll
-    for (int u = 0; u < kUnrollV; ++u) {
-      const int tl = base + u * STEP + my_row;
-      if (tl < nloop) {
-        vv[u] = E::load_nt(vbase + row_off(tl));
-      } else {
-        vv[u] = Vec{};
+      for (int u = 0; u < HV; ++u) {
+        const int tl = min(base + (half * HV + u) * STEP + my_row, nloop - 1);
+        vv[half][u] = E::load_nt(vbase + row_off(tl));
       }
+    };
+    auto accum_v = [&](int base, int half) {
+#pragma unroll
+      for (int u = 0; u < HV; ++u) {
+        const int tl = base + (half * HV + u) * STEP + my_row;
+        if (tl < nloop) {
+          float vf[EPV];
+          E::to_f32(vv[half][u], vf);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float w = s_score[tl * G + h];
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) acc[h][e] = fmaf(w, vf[e], acc[h][e]);
+          }
+        }
+      }
+    };
+    load_v(0, 0);
+    for (int base = 0; base < nloop; base += TRIPV) {
+      load_v(base, 1);
+      accum_v(base, 0);
+      if (base + TRIPV < nloop) load_v(base + TRIPV, 0);
+      accum_v(base, 1);
     }
+  }
+  if constexpr (!kPipe) {
+    for (int base = 0; base < nloop; base += STEP * kUnrollV) {
+      Vec vv[kUnrollV];
 #pragma unroll
-    for (int u = 0; u < kUnrollV; ++u) {
-      const int tl = base + u * STEP + my_row;
-      if (tl < nloop) {
-        float vf[EPV];
-        E::to_f32(vv[u], vf);
+      for (int u = 0; u < kUnrollV; ++u) {
+        const int tl = base + u * STEP + my_row;
+        vv[u] = tl < nloop ? E::load_nt(vbase + row_off(tl)) : Vec{};
+      }
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float w = s_score[tl * G + h];
+      for (int u = 0; u < kUnrollV; ++u) {
+        const int tl = base + u * STEP + my_row;
+        if (tl < nloop) {
+          float vf[EPV];
+          E::to_f32(vv[u], vf);
 #pragma unroll
-          for (int e = 0; e < EPV; ++e) acc[h][e] = fmaf(w, vf[e], acc[h][e]);
+          for (int h = 0; h < G; ++h) {
+            const float w = s_score[tl * G + h];
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) acc[h][e] = fmaf(w, vf[e], acc[h][e]);
+          }
         }
       }
     }
