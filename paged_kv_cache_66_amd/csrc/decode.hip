@@ -19,12 +19,15 @@
 //            (head_dim elements) is spread over LPT lanes, a wave covers
 //            64 / LPT rows per load; each lane dots its slice against the G
 //            query slices held in registers (v_dot2_f32_bf16 on bf16) and
-//            the LPT partial sums are combined with DPP row operations;
-//            scores (scaled by scale * log2 e) go to LDS, token-major;
+//            the LPT partial sums are combined with DPP row operations (a
+//            reduce-scatter: each lane ends with the full scores of G / LPT
+//            heads); raw scores go to LDS, token-major;
 //   phase 2  exact per-head max and sum of exp2(s - max) over the partition
 //            (no running rescale is needed because all scores are known);
 //   phase 3  V rows stream in the same way; each lane accumulates
-//            p * v for its slice of head_dim and the G heads;
+//            p * v for its slice of head_dim and the G heads (at G >= 8
+//            over half vectors, so the accumulators and the query slices
+//            fit four waves per SIMD);
 //   phase 4  partial sums are reduced across the rows of a wave (shuffles)
 //            and across waves (LDS, fixed order), then either the
 //            normalised output is written (single partition) or the
@@ -33,6 +36,7 @@
 // log-sum-exp rule. Summation order depends only on logical positions, so
 // the result is bitwise independent of where blocks sit in the pool.
 #include <mutex>
+#include <type_traits>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -43,7 +47,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kUnroll = 8;
 
 // DPP lane patterns (gfx9 encoding): quad permutations and row mirrors.
 constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
@@ -109,85 +112,134 @@ __device__ __forceinline__ float sum_lanes_16_32(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Query slice of one head held by a lane for the score pass: two 16-byte
-// vectors of the head's row, in the form the dot product wants: fp32 values
-// for fp32 caches, raw bf16 pairs for bf16 caches (products of two bf16
-// values are exact in fp32, so v_dot2_f32_bf16 computes the same partial sums
-// as widening first, with no conversion instructions).
-template <typename T> struct QSlice;
+// v + the same register of lane l ^ 32 (v_permlane32_swap, as above)
+__device__ __forceinline__ float sum_lanes_32(float v) {
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
-template <> struct QSlice<float> {
-  float v[8];
-  __device__ __forceinline__ void load(const Vec16& x0, const Vec16& x1) {
+// Query slice of one head held by a lane for the score pass: NV 16-byte
+// vectors of the head's row (the elements that match the lane's NV cache
+// vectors), in the form the dot product wants: fp32 values for fp32 caches,
+// raw bf16 pairs for bf16 caches (products of two bf16 values are exact in
+// fp32, so v_dot2_f32_bf16 computes the same partial sums as widening first,
+// with no conversion instructions).
+template <typename T, int NV> struct QSlice;
+
+template <int NV> struct QSlice<float, NV> {
+  float v[4 * NV];
+  __device__ __forceinline__ void load(int n, const Vec16& x) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[e] = __uint_as_float(x0.w[e]);
-      v[4 + e] = __uint_as_float(x1.w[e]);
-    }
+    for (int e = 0; e < 4; ++e) v[4 * n + e] = __uint_as_float(x.w[e]);
   }
-  __device__ __forceinline__ float dot(const Vec16& k0, const Vec16& k1) const {
+  __device__ __forceinline__ float dot(const Vec16 (&k)[NV]) const {
     float acc = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc = fmaf(v[e], __uint_as_float(k0.w[e]), acc);
+    for (int n = 0; n < NV; ++n)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc = fmaf(v[4 + e], __uint_as_float(k1.w[e]), acc);
+      for (int e = 0; e < 4; ++e) acc = fmaf(v[4 * n + e], __uint_as_float(k[n].w[e]), acc);
     return acc;
   }
 };
 
-template <> struct QSlice<BF16Tag> {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  uint32_t v[8];
-  __device__ __forceinline__ void load(const Vec16& x0, const Vec16& x1) {
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), acc,
+                                         false);
+}
+
+template <int NV> struct QSlice<BF16Tag, NV> {
+  uint32_t v[4 * NV];
+  __device__ __forceinline__ void load(int n, const Vec16& x) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      v[w] = x0.w[w];
-      v[4 + w] = x1.w[w];
-    }
+    for (int w = 0; w < 4; ++w) v[4 * n + w] = x.w[w];
   }
-  __device__ __forceinline__ float dot(const Vec16& k0, const Vec16& k1) const {
+  __device__ __forceinline__ float dot(const Vec16 (&k)[NV]) const {
     float acc = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v[w]),
-                                            __builtin_bit_cast(bf16x2_t, k0.w[w]), acc, false);
+    for (int n = 0; n < NV; ++n)
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v[4 + w]),
-                                            __builtin_bit_cast(bf16x2_t, k1.w[w]), acc, false);
+      for (int w = 0; w < 4; ++w) acc = dot2_bf16(v[4 * n + w], k[n].w[w], acc);
     return acc;
   }
 };
 
 // fp8 cache: the query stays bf16 (pairs as for a bf16 cache); each pair of
 // E4M3 codes is widened to a bf16 pair (exact) and fed to v_dot2_f32_bf16.
-template <> struct QSlice<Fp8Tag> {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  uint32_t v[8];
-  __device__ __forceinline__ void load(const Vec16& x0, const Vec16& x1) {
+template <int NV> struct QSlice<Fp8Tag, NV> {
+  uint32_t v[4 * NV];
+  __device__ __forceinline__ void load(int n, const Vec16& x) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      v[w] = x0.w[w];
-      v[4 + w] = x1.w[w];
-    }
+    for (int w = 0; w < 4; ++w) v[4 * n + w] = x.w[w];
   }
-  __device__ __forceinline__ static float dot2(uint32_t q, uint32_t k, float acc) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q), __builtin_bit_cast(bf16x2_t, k),
-                                           acc, false);
-  }
-  __device__ __forceinline__ float dot(const Vec8& k0, const Vec8& k1) const {
+  __device__ __forceinline__ float dot(const Vec8 (&k)[NV]) const {
     float acc = 0.f;
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      acc = dot2(v[2 * w], e4m3x2_to_bf16x2<false>(k0.w[w]), acc);
-      acc = dot2(v[2 * w + 1], e4m3x2_to_bf16x2<true>(k0.w[w]), acc);
-    }
+    for (int n = 0; n < NV; ++n)
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      acc = dot2(v[4 + 2 * w], e4m3x2_to_bf16x2<false>(k1.w[w]), acc);
-      acc = dot2(v[4 + 2 * w + 1], e4m3x2_to_bf16x2<true>(k1.w[w]), acc);
-    }
+      for (int w = 0; w < 2; ++w) {
+        acc = dot2_bf16(v[4 * n + 2 * w], e4m3x2_to_bf16x2<false>(k[n].w[w]), acc);
+        acc = dot2_bf16(v[4 * n + 2 * w + 1], e4m3x2_to_bf16x2<true>(k[n].w[w]), acc);
+      }
     return acc;
+  }
+};
+
+// Reduce-scatter of the score pass. The LPT lanes of a row each hold G
+// partial dot products; LPT is 2, 4, 8 or 16 (one DPP row at most). Step s
+// pairs lane i with lane i ^ M_s, M = (15, 7, 2, 1) cut to its last
+// log2(LPT) entries (row mirror, half-row mirror, quad swaps). While a lane
+// holds V > 1 values, a step keeps the first V / 2 and adds the partner's
+// second V / 2 to them (r_j += partner's r_{j + V/2}); once one value is left
+// the remaining steps add the partner's value. For that to add partial sums of
+// the same head, each lane orders its query heads so that register j holds
+// head head_of(i, j): follow register j forward through the halving steps
+// (the second half of the registers moves to the partner lane) and number the
+// lane it ends in by its bits above the pair-sum steps. At the end lane i
+// holds the full scores of heads (i >> TAIL) * VF + [0, VF), and the lanes that
+// differ only in their low TAIL bits hold the same values.
+template <int LPT, int G>
+struct ScoreScatter {
+  static constexpr int log2i(int x) { return x <= 1 ? 0 : 1 + log2i(x / 2); }
+  static constexpr int S = log2i(LPT);
+  static constexpr int K = S < log2i(G) ? S : log2i(G);  // halving steps
+  static constexpr int VF = G >> K;                      // values left per lane
+  static constexpr int TAIL = S - K;                     // pair-sum steps
+  static_assert((1 << S) == LPT && LPT >= 1 && LPT <= 16, "lanes per row");
+  static_assert((G & (G - 1)) == 0, "power-of-two group");
+  static constexpr int mask(int s) { return s + 4 - S == 0 ? 15 : s + 4 - S == 1 ? 7 : s + 4 - S == 2 ? 2 : 1; }
+  template <int s>
+  __device__ __forceinline__ static float from_partner(float x) {
+    constexpr int m = mask(s);
+    constexpr int ctrl = m == 15 ? kDppRowMirror : m == 7 ? kDppRowHalfMirror : m == 2 ? kDppQuadXor2 : kDppQuadXor1;
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xF, 0xF, true));
+  }
+  __device__ __forceinline__ static int head_of(int li, int j) {
+    int l = li;
+    int v = G;
+#pragma unroll
+    for (int s = 0; s < K; ++s) {
+      v /= 2;
+      if (j >= v) {
+        l ^= mask(s);
+        j -= v;
+      }
+    }
+    return (l >> TAIL) * VF + j;
+  }
+  template <int s = 0>
+  __device__ __forceinline__ static void reduce(float (&r)[G]) {
+    if constexpr (s < S) {
+      if constexpr (s < K) {
+        constexpr int half = G >> (s + 1);
+#pragma unroll
+        for (int j = 0; j < half; ++j) r[j] += from_partner<s>(r[j + half]);
+      } else {
+        r[0] += from_partner<s>(r[0]);
+      }
+      reduce<s + 1>(r);
+    }
   }
 };
 
@@ -224,25 +276,66 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   constexpr int EB = E::kBytes;      // bytes per cache element
   constexpr int QB = E::kQBytes;     // bytes per query / output element
   constexpr int VB = EPV * EB;       // bytes per lane vector (16, or 8 for fp8)
-  constexpr int kUnroll = 128 / VB;  // loads in flight per lane and loop trip
-  // score pass: a (token, kv head) row is spread over LPT1 lanes holding two
-  // vectors each (fewer lanes per row -> fewer reduction steps)
-  constexpr int LPT1 = D / (2 * EPV);
+  // score pass: a (token, kv head) row is spread over LPT1 lanes holding NV1
+  // vectors each. Two vectors per lane halve the reduction steps; at G >= 8
+  // one vector per lane halves the query registers (16-bit and fp8 caches,
+  // whose scores are combined by the reduce-scatter above; fp32 caches keep
+  // the all-lanes sum).
+  constexpr bool kScatter = !std::is_same<T, float>::value;
+  constexpr int NV1 = (kScatter && G >= 8) ? 1 : 2;
+  constexpr int LPT1 = D / (NV1 * EPV);
   constexpr int TPW1 = 64 / LPT1;
-  // 8-byte vectors (E4M3): a lane's two vectors are adjacent and travel as
-  // one 16-byte load, so a load instruction takes 128 contiguous bytes of
-  // each row; 16-byte vectors take the row in two halves
-  constexpr bool kPair = VB == 8;
+  // 8-byte vectors (E4M3) in pairs: a lane's two vectors are adjacent and
+  // travel as one 16-byte load, so a load instruction takes 128 contiguous
+  // bytes of each row; 16-byte vectors take the row in two halves
+  constexpr bool kPair = VB == 8 && NV1 == 2;
   constexpr int kSecond = kPair ? VB : LPT1 * VB;    // byte offset of the second vector
   constexpr int kFirst = kPair ? 2 * VB : VB;        // bytes between lanes' first vectors
   constexpr int STEP1 = kWaves * TPW1;
-  // value pass: LPT lanes per row, one vector each (fewer accumulators)
-  constexpr int LPT = D / EPV;       // lanes per (token, kv head) row
+  // rows per lane and loop trip: 256 bytes of loads per lane, at most 16 rows
+  constexpr int kUnroll1 = 256 / (NV1 * VB) < 16 ? 256 / (NV1 * VB) : 16;
+  // value pass: LPT lanes per row, one vector each (fewer accumulators); at
+  // G >= 8 (16-bit and fp8 caches) half a vector each (8 bytes, or 4 fp8
+  // codes), which halves the G x elements accumulators a lane keeps
+  constexpr int NVH = (kScatter && G >= 8) ? 2 : 1;
+  constexpr int EPVV = EPV / NVH;    // elements per lane in the value pass
+  constexpr int VBV = VB / NVH;      // bytes per lane and row in the value pass
+  constexpr int LPT = D / EPVV;      // lanes per (token, kv head) row
   constexpr int TPW = 64 / LPT;      // rows per wave per load
   constexpr int STEP = kWaves * TPW; // rows per workgroup per load
-  // value pass: 16 loads in flight per lane, so a 256-token partition's V
-  // rows come in one trip
-  constexpr int kUnrollV = 16;
+  // value pass: 16 vector loads in flight per lane (32 half vectors), so a
+  // 256-token partition's V rows come in one trip
+  constexpr int kUnrollV = 16 * NVH;
+  using VVec = typename std::conditional<NVH == 1, Vec, typename std::conditional<kFp8, Vec4, Vec8>::type>::type;
+  auto load_vv = [](const char* p) -> VVec {
+    if constexpr (NVH == 1) {
+      return E::load_nt(p);
+    } else if constexpr (kFp8) {
+      return Vec4{{__builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p))}};
+    } else {
+      return load8_nt(p);
+    }
+  };
+  auto vv_to_f32 = [](const VVec& v, float (&f)[EPVV]) {
+    if constexpr (NVH == 1) {
+      E::to_f32(v, f);
+    } else if constexpr (kFp8) {
+      // v_cvt_pk_f32_fp8: two codes per instruction, exact
+      typedef float f32x2_t __attribute__((ext_vector_type(2)));
+      const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v.w[0]), false);
+      const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v.w[0]), true);
+      f[0] = lo.x;
+      f[1] = lo.y;
+      f[2] = hi.x;
+      f[3] = hi.y;
+    } else {
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        f[2 * w] = bf16_lo(v.w[w]);
+        f[2 * w + 1] = bf16_hi(v.w[w]);
+      }
+    }
+  };
 
   // fused: the new row's K and V head slices, in cache format, come first
   constexpr int kNewWords = FUSED ? 2 * D * EB / 4 : 0;
@@ -334,20 +427,25 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 
   const int grp1 = lane / LPT1;
   const int li1 = lane % LPT1;
-  QSlice<T> qs[G];
+  using Scatter = ScoreScatter<(kScatter ? LPT1 : 1), G>;
+  // query head of the lane's register h: in order for the all-lanes sum, the
+  // reduce-scatter's per-lane order otherwise
+  auto qhead = [&](int h) { return kScatter ? Scatter::head_of(li1, h) : h; };
+  QSlice<T, NV1> qs[G];
   {
-    // the query elements that match the lane's two K vectors: 16 bytes each
+    // the query elements that match the lane's K vectors: 16 bytes each
     const char* qrow = q + static_cast<int64_t>(b) * q_stride_bytes;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const char* qh = qrow + static_cast<int64_t>(g * G + h) * D * QB;
-      qs[h].load(load16(qh + (li1 * kFirst / VB) * EPV * QB), load16(qh + (li1 * kFirst + kSecond) / VB * EPV * QB));
+      const char* qh = qrow + static_cast<int64_t>(g * G + qhead(h)) * D * QB;
+#pragma unroll
+      for (int n = 0; n < NV1; ++n) qs[h].load(n, load16(qh + (li1 * kFirst + n * kSecond) / VB * EPV * QB));
     }
   }
   __syncthreads();
 
   const uint64_t row_bytes = static_cast<uint64_t>(num_kv_heads) * D * EB;
-  const int64_t lane_off = static_cast<int64_t>(g) * D * EB + li * VB;
+  const int64_t lane_off = static_cast<int64_t>(g) * D * EB + li * VBV;
   const char* vbase = v_cache + lane_off;
   const int my_row = wave * TPW + grp;  // row of this lane within a load step
 
@@ -360,6 +458,39 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 
   const int nloop = new_tl >= 0 ? ntok - 1 : ntok;  // rows read from the cache
 
+  // the lane's NV1 K vectors of a row
+  const char* kbase1 = k_cache + static_cast<int64_t>(g) * D * EB + li1 * kFirst;
+  auto load_krow = [&](int tl, Vec (&k)[NV1]) {
+    const char* r = kbase1 + row_off(tl);
+    if constexpr (kPair) {
+      const Vec16 both = load16_nt(r);
+      k[0] = Vec{{both.w[0], both.w[1]}};
+      k[1] = Vec{{both.w[2], both.w[3]}};
+    } else {
+#pragma unroll
+      for (int n = 0; n < NV1; ++n) k[n] = E::load_nt(r + n * kSecond);
+    }
+  };
+  // the row's G scores from the lane's partial dots, stored by one lane per
+  // head set when `store`
+  auto score_row = [&](const Vec (&k)[NV1], int tl, bool store) {
+    float sc[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) sc[h] = qs[h].dot(k);
+    if constexpr (kScatter) {
+      Scatter::reduce(sc);
+      if (store && (li1 & ((1 << Scatter::TAIL) - 1)) == 0) {
+        float* dst = s_score + tl * G + (li1 >> Scatter::TAIL) * Scatter::VF;
+#pragma unroll
+        for (int j = 0; j < Scatter::VF; ++j) dst[j] = sc[j];
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < G; ++h) sc[h] = group_sum<LPT1>(sc[h]);
+      if (store && li1 == 0) store_scores<G>(s_score + tl * G, sc);
+    }
+  };
+
   // phase 1: raw scores q . k (the scale is applied once per score in phase 2).
   // Each trip's rows are taken in two halves with their loads in flight while
   // the other half is scored (software pipelining in the same registers): the
@@ -367,38 +498,20 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   // scored, and those of the next trip's first half before the second half
   // is. Rows past the partition load the partition's last cached row (every
   // load is unconditional, so the wait counts stay exact) and are not stored.
-  const char* kbase1 = k_cache + static_cast<int64_t>(g) * D * EB + li1 * kFirst;
   const int my_row1 = wave * TPW1 + grp1;
-  // (An E4M3 cache at G >= 8 keeps the single-buffer form below: the two
-  // halves' extra registers would cost it a wave per SIMD.)
-  constexpr bool kPipe = !(kFp8 && G >= 8);
-  if (kPipe && nloop > 0) {
-    constexpr int H1 = kUnroll / 2;
-    constexpr int TRIP1 = STEP1 * kUnroll;
-    Vec ka[2][H1], kb[2][H1];
+  if (nloop > 0) {
+    constexpr int H1 = kUnroll1 / 2;
+    constexpr int TRIP1 = STEP1 * kUnroll1;
+    Vec kv[2][H1][NV1];
     auto load_k = [&](int base, int half) {
 #pragma unroll
-      for (int u = 0; u < H1; ++u) {
-        const int tl = min(base + (half * H1 + u) * STEP1 + my_row1, nloop - 1);
-        const char* r = kbase1 + row_off(tl);
-        if constexpr (kPair) {
-          const Vec16 both = load16_nt(r);
-          ka[half][u] = Vec{{both.w[0], both.w[1]}};
-          kb[half][u] = Vec{{both.w[2], both.w[3]}};
-        } else {
-          ka[half][u] = E::load_nt(r);
-          kb[half][u] = E::load_nt(r + kSecond);
-        }
-      }
+      for (int u = 0; u < H1; ++u) load_krow(min(base + (half * H1 + u) * STEP1 + my_row1, nloop - 1), kv[half][u]);
     };
     auto score_k = [&](int base, int half) {
 #pragma unroll
       for (int u = 0; u < H1; ++u) {
         const int tl = base + (half * H1 + u) * STEP1 + my_row1;
-        float sc[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) sc[h] = group_sum<LPT1>(qs[h].dot(ka[half][u], kb[half][u]));
-        if (li1 == 0 && tl < nloop) store_scores<G>(s_score + tl * G, sc);
+        score_row(kv[half][u], tl, tl < nloop);
       }
     };
     load_k(0, 0);
@@ -409,47 +522,25 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
       score_k(base, 1);
     }
   }
-  if constexpr (!kPipe) {
-    for (int base = 0; base < nloop; base += STEP1 * kUnroll) {
-      Vec k0[kUnroll], k1[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int tl = base + u * STEP1 + my_row1;
-        if (tl < nloop) {
-          const char* r = kbase1 + row_off(tl);
-          if constexpr (kPair) {
-            const Vec16 both = load16_nt(r);
-            k0[u] = Vec{{both.w[0], both.w[1]}};
-            k1[u] = Vec{{both.w[2], both.w[3]}};
-          } else {
-            k0[u] = E::load_nt(r);
-            k1[u] = E::load_nt(r + kSecond);
-          }
-        } else {
-          k0[u] = Vec{};
-          k1[u] = Vec{};
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int tl = base + u * STEP1 + my_row1;
-        float sc[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) sc[h] = group_sum<LPT1>(qs[h].dot(k0[u], k1[u]));
-        if (li1 == 0 && tl < nloop) store_scores<G>(s_score + tl * G, sc);
-      }
-    }
-  }
   if constexpr (FUSED) {
     if (new_tl >= 0) {  // uniform: every lane joins the row-group sums
-      const Vec nk0 = *reinterpret_cast<const Vec*>(s_new + li1 * kFirst);
-      const Vec nk1 = *reinterpret_cast<const Vec*>(s_new + li1 * kFirst + kSecond);
-      float sc[G];
+      Vec nk[NV1];
 #pragma unroll
-      for (int h = 0; h < G; ++h) sc[h] = group_sum<LPT1>(qs[h].dot(nk0, nk1));
-      if (li1 == 0 && my_row1 == new_tl % STEP1) store_scores<G>(s_score + new_tl * G, sc);
+      for (int n = 0; n < NV1; ++n) nk[n] = *reinterpret_cast<const Vec*>(s_new + li1 * kFirst + n * kSecond);
+      score_row(nk, new_tl, my_row1 == new_tl % STEP1);
     }
   }
+  // The value pass's first loads go out now and land during phase 2.
+  constexpr int HV = kUnrollV / 2;
+  constexpr int TRIPV = STEP * kUnrollV;
+  VVec vv[2][HV];
+  auto load_v = [&](int base, int half) {
+#pragma unroll
+    for (int u = 0; u < HV; ++u) {
+      const int tl = min(base + (half * HV + u) * STEP + my_row, nloop - 1);
+      vv[half][u] = load_vv(vbase + row_off(tl));
+    }
+  };
   __syncthreads();
 
   // phase 2: exact max and sum of exp2(s - max) per head, in the log2 domain
@@ -514,39 +605,31 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   }
 
   // phase 3: weighted sum of V rows
-  float acc[G][EPV];
+  float acc[G][EPVV];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) acc[h][e] = 0.f;
-
-  // the same two-half pipelining as the score pass; every lane still adds
-  // its rows in increasing order
-  if (kPipe && nloop > 0) {
-    constexpr int HV = kUnrollV / 2;
-    constexpr int TRIPV = STEP * kUnrollV;
-    Vec vv[2][HV];
-    auto load_v = [&](int base, int half) {
+    for (int e = 0; e < EPVV; ++e) acc[h][e] = 0.f;
+  auto accum_row = [&](const VVec& v, int tl) {
+    float vf[EPVV];
+    vv_to_f32(v, vf);
 #pragma unroll
-      for (int u = 0; u < HV; ++u) {
-        const int tl = min(base + (half * HV + u) * STEP + my_row, nloop - 1);
-        vv[half][u] = E::load_nt(vbase + row_off(tl));
-      }
-    };
+    for (int h = 0; h < G; ++h) {
+      const float w = s_score[tl * G + h];
+#pragma unroll
+      for (int e = 0; e < EPVV; ++e) acc[h][e] = fmaf(w, vf[e], acc[h][e]);
+    }
+  };
+
+  // the same two-half pipelining as the score pass (the first half's loads
+  // were issued before phase 2); every lane still adds its rows in
+  // increasing order
+  if (nloop > 0) {
     auto accum_v = [&](int base, int half) {
 #pragma unroll
       for (int u = 0; u < HV; ++u) {
         const int tl = base + (half * HV + u) * STEP + my_row;
-        if (tl < nloop) {
-          float vf[EPV];
-          E::to_f32(vv[half][u], vf);
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float w = s_score[tl * G + h];
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) acc[h][e] = fmaf(w, vf[e], acc[h][e]);
-          }
-        }
+        if (tl < nloop) accum_row(vv[half][u], tl);
       }
     };
     load_v(0, 0);
@@ -557,52 +640,22 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
       accum_v(base, 1);
     }
   }
-  if constexpr (!kPipe) {
-    for (int base = 0; base < nloop; base += STEP * kUnrollV) {
-      Vec vv[kUnrollV];
-#pragma unroll
-      for (int u = 0; u < kUnrollV; ++u) {
-        const int tl = base + u * STEP + my_row;
-        vv[u] = tl < nloop ? E::load_nt(vbase + row_off(tl)) : Vec{};
-      }
-#pragma unroll
-      for (int u = 0; u < kUnrollV; ++u) {
-        const int tl = base + u * STEP + my_row;
-        if (tl < nloop) {
-          float vf[EPV];
-          E::to_f32(vv[u], vf);
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float w = s_score[tl * G + h];
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) acc[h][e] = fmaf(w, vf[e], acc[h][e]);
-          }
-        }
-      }
-    }
-  }
   if constexpr (FUSED) {
     // the new row is this lane's last row, so it is added last, as in pa_decode
-    if (new_tl >= 0 && my_row == new_tl % STEP) {
-      float vf[EPV];
-      E::to_f32(*reinterpret_cast<const Vec*>(s_new + row_bytes_h + li * VB), vf);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float w = s_score[new_tl * G + h];
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) acc[h][e] = fmaf(w, vf[e], acc[h][e]);
-      }
-    }
+    if (new_tl >= 0 && my_row == new_tl % STEP)
+      accum_row(*reinterpret_cast<const VVec*>(s_new + row_bytes_h + li * VBV), new_tl);
   }
 
   // phase 4: reduce over the rows of a wave, then over waves in fixed order
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) {
+    for (int e = 0; e < EPVV; ++e) {
       float v = acc[h][e];
       if constexpr (LPT == 16) {
         v = sum_lanes_16_32(v);  // the rows of a wave: lanes l, l ^ 16, l ^ 32, l ^ 48
+      } else if constexpr (LPT == 32) {
+        v = sum_lanes_32(v);     // the rows of a wave: lanes l, l ^ 32
       } else {
 #pragma unroll
         for (int off = LPT; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
@@ -615,7 +668,7 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) s_red[(wave * G + h) * D + li * EPV + e] = acc[h][e];
+      for (int e = 0; e < EPVV; ++e) s_red[(wave * G + h) * D + li * EPVV + e] = acc[h][e];
   }
   __syncthreads();
 
@@ -648,61 +701,96 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 
 // Log-sum-exp merge of the partition partials of one (sequence, query head):
 //   M = max_p m_p,  L = sum_p l_p 2^(m_p - M),  o = sum_p 2^(m_p - M) acc_p / L.
-// One wave per (sequence, query head): the lanes share the per-partition
-// statistics, then every lane owns D / 64 output elements and sums the
-// partials in partition order (fixed, so the result is reproducible), with
-// the loads of several partitions in flight at once.
+// One 256-thread workgroup per (sequence, query head). M and L: each thread
+// takes every 256th partition, then the workgroup combines them. The
+// weighted sum: D / 4 lanes cover a partial row with 16-byte loads, and the
+// 256 / (D / 4) lane groups take every group-count-th partition, in
+// increasing order, four loads in flight; the groups' sums then combine in
+// group order. Every order is fixed, so the result is reproducible.
 template <typename T, int D>
-__global__ void __launch_bounds__(64) decode_reduce_kernel(
+__global__ void __launch_bounds__(kThreads) decode_reduce_kernel(
     void* __restrict__ out, const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
     const int32_t* __restrict__ context_lens, int32_t max_ctx, int32_t num_q_heads,
     int32_t partition, int32_t num_partitions) {
-  constexpr int PER = D / 64;
-  constexpr int kBatch = 8;
+  constexpr int LPR = D / 4;            // lanes per partial row
+  constexpr int NG = kThreads / LPR;    // partition groups
+  constexpr int kBatch = 4;
+  __shared__ float s_wred[2 * kWaves];
+  __shared__ float4 s_grp[NG][LPR];
   const int h = blockIdx.x;
   const int b = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int n = min(context_lens[b], max_ctx);  // as in the partition kernel
   const int np = (n + partition - 1) / partition;
   const int64_t slot0 = (static_cast<int64_t>(b) * num_q_heads + h) * num_partitions;
   const float* ml = ws_ml + slot0 * 2;
-  const float* acc = ws_acc + slot0 * D + lane;
-  float o[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) o[k] = 0.f;
-  if (np > 0) {
+  const int grp = tid / LPR;
+  const int c = tid % LPR;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (np > 0) {  // uniform
     float m = -INFINITY;
-    for (int pp = lane; pp < np; pp += 64) m = fmaxf(m, ml[2 * pp]);
-    const float M = wave_max(m);
-    float lsum = 0.f;
-    for (int pp = lane; pp < np; pp += 64) lsum += ml[2 * pp + 1] * exp2f(ml[2 * pp] - M);
-    const float L = wave_sum(lsum);
-    for (int p0 = 0; p0 < np; p0 += kBatch) {
+    for (int pp = tid; pp < np; pp += kThreads) m = fmaxf(m, ml[2 * pp]);
+    m = wave_max(m);
+    if (lane == 0) s_wred[wave] = m;
+    __syncthreads();
+    float M = s_wred[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_wred[w]);
+    float l = 0.f;
+    for (int pp = tid; pp < np; pp += kThreads) l += ml[2 * pp + 1] * exp2f(ml[2 * pp] - M);
+    l = wave_sum(l);
+    if (lane == 0) s_wred[kWaves + wave] = l;
+
+    const float4* acc = reinterpret_cast<const float4*>(ws_acc + slot0 * D) + c;
+    for (int p0 = grp; p0 < np; p0 += NG * kBatch) {
       float w[kBatch];
-      float a[kBatch][PER];
+      float4 a[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        const int pp = p0 + u;
+        const int pp = p0 + u * NG;
         w[u] = pp < np ? exp2f(ml[2 * pp] - M) : 0.f;
-#pragma unroll
-        for (int k = 0; k < PER; ++k) a[u][k] = pp < np ? acc[static_cast<int64_t>(pp) * D + k * 64] : 0.f;
+        a[u] = pp < np ? acc[static_cast<int64_t>(pp) * LPR] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-#pragma unroll
-        for (int k = 0; k < PER; ++k) o[k] = fmaf(w[u], a[u][k], o[k]);
+      for (int u = 0; u < kBatch; ++u) {
+        o.x = fmaf(w[u], a[u].x, o.x);
+        o.y = fmaf(w[u], a[u].y, o.y);
+        o.z = fmaf(w[u], a[u].z, o.z);
+        o.w = fmaf(w[u], a[u].w, o.w);
+      }
     }
-    const float inv = 1.f / L;
+    s_grp[grp][c] = o;
+    __syncthreads();
+    if (grp == 0) {
+      float L = s_wred[kWaves];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) o[k] *= inv;
+      for (int w = 1; w < kWaves; ++w) L += s_wred[kWaves + w];
+#pragma unroll
+      for (int k = 1; k < NG; ++k) {
+        const float4 x = s_grp[k][c];
+        o.x += x.x;
+        o.y += x.y;
+        o.z += x.z;
+        o.w += x.w;
+      }
+      const float inv = 1.f / L;
+      o.x *= inv;
+      o.y *= inv;
+      o.z *= inv;
+      o.w *= inv;
+    }
   }
-  const int64_t ob = (static_cast<int64_t>(b) * num_q_heads + h) * D;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
+  if (grp == 0) {
+    const int64_t ob = (static_cast<int64_t>(b) * num_q_heads + h) * D + c * 4;
     if constexpr (Elem<T>::kQBytes == 2) {
-      reinterpret_cast<uint16_t*>(out)[ob + k * 64 + lane] = static_cast<uint16_t>(f32_to_bf16_bits(o[k]));
+      uint2 pk;
+      pk.x = f32_to_bf16_bits(o.x) | (f32_to_bf16_bits(o.y) << 16);
+      pk.y = f32_to_bf16_bits(o.z) | (f32_to_bf16_bits(o.w) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + ob) = pk;
     } else {
-      reinterpret_cast<float*>(out)[ob + k * 64 + lane] = o[k];
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + ob) = o;
     }
   }
 }
@@ -732,7 +820,7 @@ hipError_t launch_decode_typed(const DecodeArgs& a, hipStream_t stream) {
                      a.k_scale, a.v_scale);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.num_partitions == 1) return err;
-  hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3(a.num_q_heads, a.num_seqs), dim3(64), 0,
+  hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3(a.num_q_heads, a.num_seqs), dim3(kThreads), 0,
                      stream, a.out, a.ws_acc, a.ws_ml, a.context_lens, max_ctx, a.num_q_heads,
                      a.partition, a.num_partitions);
   return hipGetLastError();

@@ -29,6 +29,11 @@ __device__ __forceinline__ void store16(void* p, const Vec16& v) {
   *reinterpret_cast<Vec16*>(p) = v;
 }
 
+// 4-byte vector: four fp8 cache elements.
+struct alignas(4) Vec4 {
+  uint32_t w[1];
+};
+
 // 8-byte vector: eight fp8 cache elements.
 struct alignas(8) Vec8 {
   uint32_t w[2];
