@@ -701,21 +701,23 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 
 // Log-sum-exp merge of the partition partials of one (sequence, query head):
 //   M = max_p m_p,  L = sum_p l_p 2^(m_p - M),  o = sum_p 2^(m_p - M) acc_p / L.
-// One 256-thread workgroup per (sequence, query head). M and L: each thread
-// takes every 256th partition, then the workgroup combines them. The
-// weighted sum: D / 4 lanes cover a partial row with 16-byte loads, and the
-// 256 / (D / 4) lane groups take every group-count-th partition, in
-// increasing order, four loads in flight; the groups' sums then combine in
-// group order. Every order is fixed, so the result is reproducible.
-template <typename T, int D>
-__global__ void __launch_bounds__(kThreads) decode_reduce_kernel(
+// One workgroup of NT threads (64, or 256 for long tables) per (sequence,
+// query head). M and L: each thread takes every NT-th partition, then the
+// workgroup combines them. The weighted sum: D / 4 lanes cover a partial row
+// with 16-byte loads, and the NT / (D / 4) lane groups take every
+// group-count-th partition, in increasing order, four loads in flight; the
+// groups' sums then combine in group order. Every order is fixed, so the
+// result is reproducible.
+template <typename T, int D, int NT>
+__global__ void __launch_bounds__(NT) decode_reduce_kernel(
     void* __restrict__ out, const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
     const int32_t* __restrict__ context_lens, int32_t max_ctx, int32_t num_q_heads,
     int32_t partition, int32_t num_partitions) {
   constexpr int LPR = D / 4;            // lanes per partial row
-  constexpr int NG = kThreads / LPR;    // partition groups
+  constexpr int NG = NT / LPR;          // partition groups
+  constexpr int NW = NT / 64;           // waves
   constexpr int kBatch = 4;
-  __shared__ float s_wred[2 * kWaves];
+  __shared__ float s_wred[2 * NW];
   __shared__ float4 s_grp[NG][LPR];
   const int h = blockIdx.x;
   const int b = blockIdx.y;
@@ -731,17 +733,17 @@ __global__ void __launch_bounds__(kThreads) decode_reduce_kernel(
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   if (np > 0) {  // uniform
     float m = -INFINITY;
-    for (int pp = tid; pp < np; pp += kThreads) m = fmaxf(m, ml[2 * pp]);
+    for (int pp = tid; pp < np; pp += NT) m = fmaxf(m, ml[2 * pp]);
     m = wave_max(m);
     if (lane == 0) s_wred[wave] = m;
     __syncthreads();
     float M = s_wred[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_wred[w]);
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_wred[w]);
     float l = 0.f;
-    for (int pp = tid; pp < np; pp += kThreads) l += ml[2 * pp + 1] * exp2f(ml[2 * pp] - M);
+    for (int pp = tid; pp < np; pp += NT) l += ml[2 * pp + 1] * exp2f(ml[2 * pp] - M);
     l = wave_sum(l);
-    if (lane == 0) s_wred[kWaves + wave] = l;
+    if (lane == 0) s_wred[NW + wave] = l;
 
     const float4* acc = reinterpret_cast<const float4*>(ws_acc + slot0 * D) + c;
     for (int p0 = grp; p0 < np; p0 += NG * kBatch) {
@@ -764,9 +766,9 @@ __global__ void __launch_bounds__(kThreads) decode_reduce_kernel(
     s_grp[grp][c] = o;
     __syncthreads();
     if (grp == 0) {
-      float L = s_wred[kWaves];
+      float L = s_wred[NW];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) L += s_wred[kWaves + w];
+      for (int w = 1; w < NW; ++w) L += s_wred[NW + w];
 #pragma unroll
       for (int k = 1; k < NG; ++k) {
         const float4 x = s_grp[k][c];
@@ -820,9 +822,17 @@ hipError_t launch_decode_typed(const DecodeArgs& a, hipStream_t stream) {
                      a.k_scale, a.v_scale);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.num_partitions == 1) return err;
-  hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3(a.num_q_heads, a.num_seqs), dim3(kThreads), 0,
-                     stream, a.out, a.ws_acc, a.ws_ml, a.context_lens, max_ctx, a.num_q_heads,
-                     a.partition, a.num_partitions);
+  // a workgroup of 256 threads pays off once a head has many partials;
+  // otherwise 64 (its barriers and LDS combine cost more than they save)
+  if (a.num_partitions >= 64) {
+    hipLaunchKernelGGL((decode_reduce_kernel<T, D, 256>), dim3(a.num_q_heads, a.num_seqs), dim3(256), 0,
+                       stream, a.out, a.ws_acc, a.ws_ml, a.context_lens, max_ctx, a.num_q_heads,
+                       a.partition, a.num_partitions);
+  } else {
+    hipLaunchKernelGGL((decode_reduce_kernel<T, D, 64>), dim3(a.num_q_heads, a.num_seqs), dim3(64), 0,
+                       stream, a.out, a.ws_acc, a.ws_ml, a.context_lens, max_ctx, a.num_q_heads,
+                       a.partition, a.num_partitions);
+  }
   return hipGetLastError();
 }
 
