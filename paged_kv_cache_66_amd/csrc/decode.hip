@@ -48,6 +48,11 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
+// Fourth word of a raw buffer resource (untyped 32-bit data format) and the
+// cache-policy argument of a non-temporal buffer load.
+constexpr int kRawBufferFlags = 0x00020000;
+constexpr int kLoadNt = 2;
+
 // DPP lane patterns (gfx9 encoding): quad permutations and row mirrors.
 constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
@@ -258,7 +263,7 @@ struct ScoreScatter {
 // k_scale / v_scale first) and takes the row from the new key/value inputs
 // instead of the cache. The caller guarantees that slot is the slot of
 // position context_len - 1 (or -1: no store, row read from the cache).
-template <typename T, int D, int G, bool FUSED>
+template <typename T, int D, int G, bool FUSED, bool BT>
 __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
     void* __restrict__ out, const char* __restrict__ q, int64_t q_stride_bytes,
     char* __restrict__ k_cache, char* __restrict__ v_cache,
@@ -458,6 +463,28 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
 
   const int nloop = new_tl >= 0 ? ntok - 1 : ntok;  // rows read from the cache
 
+  // BT (block trips): the launch guarantees that every half-trip of rows
+  // (128 or 256 rows, starting at a multiple of its length from the partition
+  // start) lies inside one block: blocks of at least 256 rows, partitions a
+  // multiple of 256. A half-trip's addresses are then that block's base, plus
+  // a lane offset fixed for the whole kernel, plus a per-row step that is the
+  // same for every lane, so it loads through a buffer resource on the block
+  // (one block-id lookup) with the step in a scalar register, instead of a
+  // block lookup and a 64-bit address per row and lane. A half-trip that
+  // starts at or past the last cached row takes the block of that row (its
+  // rows stay inside an allocated block and are never used); rows past the
+  // last cached one inside a half-trip are loaded and never used.
+  auto block_rsrc = [&](const char* head_base, int b0) -> __amdgpu_buffer_rsrc_t {
+    const uint32_t pos = static_cast<uint32_t>(t0 + b0);
+    const uint32_t last = static_cast<uint32_t>(t0 + nloop - 1);
+    const uint32_t bi = min(pos >> log2_bs, last >> log2_bs) - static_cast<uint32_t>(jb0);
+    const uint32_t blk = __builtin_amdgcn_readfirstlane(s_ids[bi]);
+    const uint64_t row0 = (static_cast<uint64_t>(blk) << log2_bs) + (pos & bs_mask);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(head_base + row0 * row_bytes), 0, 0x7fffffff,
+                                             kRawBufferFlags);
+  };
+  const uint32_t row_bytes32 = static_cast<uint32_t>(row_bytes);
+
   // the lane's NV1 K vectors of a row
   const char* kbase1 = k_cache + static_cast<int64_t>(g) * D * EB + li1 * kFirst;
   auto load_krow = [&](int tl, Vec (&k)[NV1]) {
@@ -503,9 +530,33 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
     constexpr int H1 = kUnroll1 / 2;
     constexpr int TRIP1 = STEP1 * kUnroll1;
     Vec kv[2][H1][NV1];
+    const char* khead = k_cache + static_cast<int64_t>(g) * D * EB;
+    const uint32_t klane = static_cast<uint32_t>(my_row1) * row_bytes32 + static_cast<uint32_t>(li1 * kFirst);
     auto load_k = [&](int base, int half) {
+      const int b0 = base + half * H1 * STEP1;
+      if constexpr (BT) {
+        const __amdgpu_buffer_rsrc_t r = block_rsrc(khead, b0);
 #pragma unroll
-      for (int u = 0; u < H1; ++u) load_krow(min(base + (half * H1 + u) * STEP1 + my_row1, nloop - 1), kv[half][u]);
+        for (int u = 0; u < H1; ++u) {
+          const uint32_t so = static_cast<uint32_t>(u * STEP1) * row_bytes32;
+          if constexpr (kPair) {
+            const Vec16 both = __builtin_bit_cast(Vec16, __builtin_amdgcn_raw_buffer_load_b128(r, klane, so, kLoadNt));
+            kv[half][u][0] = Vec{{both.w[0], both.w[1]}};
+            kv[half][u][1] = Vec{{both.w[2], both.w[3]}};
+          } else if constexpr (kFp8) {
+#pragma unroll
+            for (int n = 0; n < NV1; ++n)
+              kv[half][u][n] = __builtin_bit_cast(Vec, __builtin_amdgcn_raw_buffer_load_b64(r, klane, so + n * kSecond, kLoadNt));
+          } else {
+#pragma unroll
+            for (int n = 0; n < NV1; ++n)
+              kv[half][u][n] = __builtin_bit_cast(Vec, __builtin_amdgcn_raw_buffer_load_b128(r, klane, so + n * kSecond, kLoadNt));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < H1; ++u) load_krow(min(b0 + u * STEP1 + my_row1, nloop - 1), kv[half][u]);
+      }
     };
     auto score_k = [&](int base, int half) {
 #pragma unroll
@@ -530,15 +581,30 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
       score_row(nk, new_tl, my_row1 == new_tl % STEP1);
     }
   }
-  // The value pass's first loads go out now and land during phase 2.
+  // the value pass's loads (phase 3)
   constexpr int HV = kUnrollV / 2;
   constexpr int TRIPV = STEP * kUnrollV;
   VVec vv[2][HV];
+  const char* vhead = v_cache + static_cast<int64_t>(g) * D * EB;
+  const uint32_t vlane = static_cast<uint32_t>(my_row) * row_bytes32 + static_cast<uint32_t>(li * VBV);
   auto load_v = [&](int base, int half) {
+    const int b0 = base + half * HV * STEP;
+    if constexpr (BT) {
+      const __amdgpu_buffer_rsrc_t r = block_rsrc(vhead, b0);
 #pragma unroll
-    for (int u = 0; u < HV; ++u) {
-      const int tl = min(base + (half * HV + u) * STEP + my_row, nloop - 1);
-      vv[half][u] = load_vv(vbase + row_off(tl));
+      for (int u = 0; u < HV; ++u) {
+        const uint32_t so = static_cast<uint32_t>(u * STEP) * row_bytes32;
+        if constexpr (sizeof(VVec) == 16) {
+          vv[half][u] = __builtin_bit_cast(VVec, __builtin_amdgcn_raw_buffer_load_b128(r, vlane, so, kLoadNt));
+        } else if constexpr (sizeof(VVec) == 8) {
+          vv[half][u] = __builtin_bit_cast(VVec, __builtin_amdgcn_raw_buffer_load_b64(r, vlane, so, kLoadNt));
+        } else {
+          vv[half][u] = __builtin_bit_cast(VVec, __builtin_amdgcn_raw_buffer_load_b32(r, vlane, so, kLoadNt));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < HV; ++u) vv[half][u] = load_vv(vbase + row_off(min(b0 + u * STEP + my_row, nloop - 1)));
     }
   };
   __syncthreads();
@@ -799,6 +865,10 @@ __global__ void __launch_bounds__(NT) decode_reduce_kernel(
 
 template <typename T, int D, int G, bool FUSED>
 hipError_t launch_decode_typed(const DecodeArgs& a, hipStream_t stream) {
+  // block trips (see the kernel): blocks of 256+ rows and partitions a
+  // multiple of 256; measured worth it at G >= 8 (16-bit and fp8 caches)
+  constexpr bool kBtKernels = G >= 8 && !std::is_same<T, float>::value;
+  const bool bt = kBtKernels && a.block_size >= 256 && a.partition % 256 == 0;
   constexpr int QB = Elem<T>::kQBytes;
   int log2_bs = 0;
   while ((1 << log2_bs) < a.block_size) ++log2_bs;
@@ -811,15 +881,24 @@ hipError_t launch_decode_typed(const DecodeArgs& a, hipStream_t stream) {
   const int64_t table_rows = static_cast<int64_t>(a.max_blocks) << log2_bs;
   const int32_t max_ctx = static_cast<int32_t>(table_rows < INT32_MAX ? table_rows : INT32_MAX);
   dim3 grid(a.num_partitions * a.num_kv_heads * a.num_seqs);
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, G, FUSED>), grid, dim3(kThreads), lds, stream,
-                     a.out, static_cast<const char*>(a.q), a.q_stride * QB,
-                     static_cast<char*>(const_cast<void*>(a.k_cache)),
-                     static_cast<char*>(const_cast<void*>(a.v_cache)), a.block_tables, a.max_blocks,
-                     a.context_lens, max_ctx, a.num_q_heads, a.num_kv_heads, log2_bs, scale_log2, a.partition,
-                     a.num_partitions, score_words, a.ws_acc, a.ws_ml,
-                     static_cast<const char*>(a.new_k), a.new_k_stride * QB,
-                     static_cast<const char*>(a.new_v), a.new_v_stride * QB, a.slot_mapping,
-                     a.k_scale, a.v_scale);
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), lds, stream, a.out, static_cast<const char*>(a.q),
+                       a.q_stride * QB, static_cast<char*>(const_cast<void*>(a.k_cache)),
+                       static_cast<char*>(const_cast<void*>(a.v_cache)), a.block_tables, a.max_blocks,
+                       a.context_lens, max_ctx, a.num_q_heads, a.num_kv_heads, log2_bs, scale_log2, a.partition,
+                       a.num_partitions, score_words, a.ws_acc, a.ws_ml, static_cast<const char*>(a.new_k),
+                       a.new_k_stride * QB, static_cast<const char*>(a.new_v), a.new_v_stride * QB,
+                       a.slot_mapping, a.k_scale, a.v_scale);
+  };
+  if constexpr (kBtKernels) {
+    if (bt) {
+      launch(decode_partition_kernel<T, D, G, FUSED, true>);
+    } else {
+      launch(decode_partition_kernel<T, D, G, FUSED, false>);
+    }
+  } else {
+    launch(decode_partition_kernel<T, D, G, FUSED, false>);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.num_partitions == 1) return err;
   // a workgroup of 256 threads pays off once a head has many partials;

@@ -305,6 +305,42 @@ def test_store_decode_matches_separate_calls(dtype, d, g, partition):
     assert_attention_close(widen_host(to_host(fused, w.dtype), w.dtype), ref, w.dtype, "fused")
 
 
+# Contexts that end inside, at and just past the 128-row half-trips and the
+# 256-row blocks; 1 and 100 end before the first half-trip does.
+BLOCK_TRIP_CTX = [1, 100, 127, 128, 129, 255, 256, 257, 300, 511, 512, 700, 1023, 1024, 1025, 2000]
+
+
+@pytest.mark.parametrize("g,hkv,d,part", [
+    (8, 2, 128, 256), (8, 2, 128, 512), (8, 2, 128, 1024), (8, 2, 64, 256),
+    (16, 1, 128, 256), (16, 1, 128, 512),
+])
+def test_decode_block_trips(g, hkv, d, part):
+    """Blocks of 256 rows and partitions that are multiples of 256: at G >= 8
+    the launch takes the kernel that loads each half-trip of rows through one
+    block lookup. Split-K launches against the oracle, and the fused call
+    against the two calls bit for bit."""
+    import torch
+    w = wl.custom_decode(BLOCK_TRIP_CTX, block_size=256, num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d,
+                         dtype="bf16", seed=g * 7 + d + part, width=wl.num_blocks_for(2000, 256) + 1)
+    run_small(w, part)
+    t = wl.make_host_tensors(w)
+    dev = _device_inputs(w, t)
+    fused = _fused_vs_separate(w, {"q": dev["q"], "k": dev["k"], "v": dev["v"],
+                                   "k_cache": dev["k_cache"], "v_cache": dev["v_cache"]}, part)
+    kc, vc = t["k_cache"].copy(), t["v_cache"].copy()
+    oracle.store_kvcache(t["k"], t["v"], kc, vc, w.slot_mapping)
+    ref = oracle.decode(t["q"], kc, vc, w.block_tables, w.context_lens, w.scale, w.dtype)
+    assert_attention_close(widen_host(to_host(fused, w.dtype), w.dtype), ref, w.dtype, "fused")
+
+
+def test_decode_block_trips_single_pass():
+    """The block-trip kernel as a one-pass launch (the partition covers the
+    whole table row: no merge)."""
+    w = wl.custom_decode([1, 129, 256, 300, 511], block_size=256, num_q_heads=16, num_kv_heads=2,
+                         head_dim=128, dtype="bf16", seed=41, width=2)
+    run_small(w, 512)
+
+
 @pytest.mark.parametrize("name", ["qwen3-0.6b-decode", "8b-decode-bs16", "8b-decode-bs256", "long-context-decode"])
 def test_store_decode_full_size(name):
     import torch

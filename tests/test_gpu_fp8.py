@@ -296,6 +296,18 @@ def test_decode_fp8_block_sizes(bs, ctx):
     run_decode_fp8(wl.with_fp8_cache(w, 0.03, 0.011), 0)
 
 
+@pytest.mark.parametrize("g,hkv,part", [(8, 2, 256), (8, 2, 1024), (16, 1, 512)])
+def test_decode_fp8_block_trips(g, hkv, part):
+    """fp8 caches with blocks of 256 rows and partitions that are multiples
+    of 256 at G >= 8 (the block-trip kernel): contexts ending inside, at and
+    just past half-trips and blocks; two calls and the fused call against the
+    oracle, and against each other bit for bit."""
+    ctx = [1, 100, 127, 128, 129, 255, 256, 257, 300, 511, 512, 700, 1023, 1024, 1025, 2000]
+    w = wl.custom_decode(ctx, block_size=256, num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=128,
+                         dtype="bf16", seed=g + part, width=wl.num_blocks_for(2000, 256) + 1)
+    run_decode_fp8(wl.with_fp8_cache(w, 0.02, 0.015), part)
+
+
 def test_decode_fp8_small_scale_many_subnormals():
     """k_scale and v_scale of 8: most N(0, 1) inputs land on subnormal or
     small codes, so the store's rounding and the dequantisation of small
