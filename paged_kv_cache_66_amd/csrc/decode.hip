@@ -303,6 +303,7 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   // G >= 8 (16-bit and fp8 caches) half a vector each (8 bytes, or 4 fp8
   // codes), which halves the G x elements accumulators a lane keeps
   constexpr int NVH = (kScatter && G >= 8) ? 2 : 1;
+  constexpr bool kPairV = NVH == 2 && BT;  // value pass in row pairs (see accum_pair)
   constexpr int EPVV = EPV / NVH;    // elements per lane in the value pass
   constexpr int VBV = VB / NVH;      // bytes per lane and row in the value pass
   constexpr int LPT = D / EPVV;      // lanes per (token, kv head) row
@@ -462,6 +463,11 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   };
 
   const int nloop = new_tl >= 0 ? ntok - 1 : ntok;  // rows read from the cache
+  // the partition's row of position n - 1 (or -1), and the rows the value
+  // pass takes in its loop: in row pairs that last row is added after the
+  // loop in both the fused call and pa_decode
+  const int last_tl = t1 == n ? ntok - 1 : -1;
+  const int vloop = (kPairV && last_tl >= 0) ? ntok - 1 : nloop;
 
   // BT (block trips): the launch guarantees that every half-trip of rows
   // (128 or 256 rows, starting at a multiple of its length from the partition
@@ -676,6 +682,34 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < EPVV; ++e) acc[h][e] = 0.f;
+  // G >= 8: a lane's consecutive rows tl and tl + STEP in one v_dot2 per
+  // element and head, with bf16 weights: (p(tl), p(tl + STEP)) . (v(tl),
+  // v(tl + STEP)). The V pairs come from byte permutes (and, for E4M3 codes,
+  // the exact widening to bf16); the weights are rounded to bf16 here.
+  auto accum_pair = [&](const VVec& a, const VVec& b, int tl) {
+    uint32_t vp[EPVV];
+    if constexpr (kFp8) {
+      const uint32_t w0 = __builtin_amdgcn_perm(b.w[0], a.w[0], 0x05010400u);
+      const uint32_t w1 = __builtin_amdgcn_perm(b.w[0], a.w[0], 0x07030602u);
+      vp[0] = e4m3x2_to_bf16x2<false>(w0);
+      vp[1] = e4m3x2_to_bf16x2<true>(w0);
+      vp[2] = e4m3x2_to_bf16x2<false>(w1);
+      vp[3] = e4m3x2_to_bf16x2<true>(w1);
+    } else {
+#pragma unroll
+      for (int w = 0; w < EPVV / 2; ++w) {
+        vp[2 * w] = __builtin_amdgcn_perm(b.w[w], a.w[w], 0x05040100u);
+        vp[2 * w + 1] = __builtin_amdgcn_perm(b.w[w], a.w[w], 0x07060302u);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const bf16x2_t pp = {static_cast<__bf16>(s_score[tl * G + h]), static_cast<__bf16>(s_score[(tl + STEP) * G + h])};
+      const uint32_t pw = __builtin_bit_cast(uint32_t, pp);
+#pragma unroll
+      for (int e = 0; e < EPVV; ++e) acc[h][e] = dot2_bf16(pw, vp[e], acc[h][e]);
+    }
+  };
   auto accum_row = [&](const VVec& v, int tl) {
     float vf[EPVV];
     vv_to_f32(v, vf);
@@ -692,10 +726,22 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   // increasing order
   if (nloop > 0) {
     auto accum_v = [&](int base, int half) {
+      if constexpr (kPairV) {
 #pragma unroll
-      for (int u = 0; u < HV; ++u) {
-        const int tl = base + (half * HV + u) * STEP + my_row;
-        if (tl < nloop) accum_row(vv[half][u], tl);
+        for (int u = 0; u < HV; u += 2) {
+          const int tl = base + (half * HV + u) * STEP + my_row;
+          if (tl + STEP < vloop) {
+            accum_pair(vv[half][u], vv[half][u + 1], tl);
+          } else if (tl < vloop) {
+            accum_row(vv[half][u], tl);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < HV; ++u) {
+          const int tl = base + (half * HV + u) * STEP + my_row;
+          if (tl < nloop) accum_row(vv[half][u], tl);
+        }
       }
     };
     load_v(0, 0);
@@ -706,7 +752,19 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
       accum_v(base, 1);
     }
   }
-  if constexpr (FUSED) {
+  if constexpr (kPairV) {
+    // the sequence's last row is added last, alone, in both the fused call
+    // (from LDS) and pa_decode (from the cache), so the two sum alike
+    if (last_tl >= 0 && my_row == last_tl % STEP) {
+      VVec lv;
+      if (FUSED && new_tl >= 0) {
+        lv = *reinterpret_cast<const VVec*>(s_new + row_bytes_h + li * VBV);
+      } else {
+        lv = load_vv(vbase + row_off(last_tl));
+      }
+      accum_row(lv, last_tl);
+    }
+  } else if constexpr (FUSED) {
     // the new row is this lane's last row, so it is added last, as in pa_decode
     if (new_tl >= 0 && my_row == new_tl % STEP)
       accum_row(*reinterpret_cast<const VVec*>(s_new + row_bytes_h + li * VBV), new_tl);
