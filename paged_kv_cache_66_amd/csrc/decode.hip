@@ -137,6 +137,7 @@ template <int NV> struct QSlice<float, NV> {
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[4 * n + e] = __uint_as_float(x.w[e]);
   }
+  template <bool kZeroStart = false>
   __device__ __forceinline__ float dot(const Vec16 (&k)[NV]) const {
     float acc = 0.f;
 #pragma unroll
@@ -154,18 +155,30 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
                                          false);
 }
 
+// The first product of a chain: v_dot2_f32_bf16 with the inline constant 0
+// as the addend. (Left to itself the compiler starts every chain with a
+// v_mov of 0 into the accumulator of the two-operand v_dot2c form: one more
+// vector instruction per chain, i.e. per head and row in the score pass.)
+__device__ __forceinline__ float dot2_bf16_first(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 template <int NV> struct QSlice<BF16Tag, NV> {
   uint32_t v[4 * NV];
   __device__ __forceinline__ void load(int n, const Vec16& x) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) v[4 * n + w] = x.w[w];
   }
+  template <bool kZeroStart = false>
   __device__ __forceinline__ float dot(const Vec16 (&k)[NV]) const {
-    float acc = 0.f;
+    float acc = kZeroStart ? dot2_bf16_first(v[0], k[0].w[0]) : dot2_bf16(v[0], k[0].w[0], 0.f);
 #pragma unroll
     for (int n = 0; n < NV; ++n)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) acc = dot2_bf16(v[4 * n + w], k[n].w[w], acc);
+      for (int w = 0; w < 4; ++w)
+        if (n > 0 || w > 0) acc = dot2_bf16(v[4 * n + w], k[n].w[w], acc);
     return acc;
   }
 };
@@ -178,13 +191,15 @@ template <int NV> struct QSlice<Fp8Tag, NV> {
 #pragma unroll
     for (int w = 0; w < 4; ++w) v[4 * n + w] = x.w[w];
   }
+  template <bool kZeroStart = false>
   __device__ __forceinline__ float dot(const Vec8 (&k)[NV]) const {
-    float acc = 0.f;
+    const uint32_t k0 = e4m3x2_to_bf16x2<false>(k[0].w[0]);
+    float acc = kZeroStart ? dot2_bf16_first(v[0], k0) : dot2_bf16(v[0], k0, 0.f);
 #pragma unroll
     for (int n = 0; n < NV; ++n)
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
-        acc = dot2_bf16(v[4 * n + 2 * w], e4m3x2_to_bf16x2<false>(k[n].w[w]), acc);
+        if (n > 0 || w > 0) acc = dot2_bf16(v[4 * n + 2 * w], e4m3x2_to_bf16x2<false>(k[n].w[w]), acc);
         acc = dot2_bf16(v[4 * n + 2 * w + 1], e4m3x2_to_bf16x2<true>(k[n].w[w]), acc);
       }
     return acc;
@@ -264,7 +279,7 @@ struct ScoreScatter {
 // instead of the cache. The caller guarantees that slot is the slot of
 // position context_len - 1 (or -1: no store, row read from the cache).
 template <typename T, int D, int G, bool FUSED, bool BT>
-__global__ void __launch_bounds__(kThreads) decode_partition_kernel(
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BT && G == 8 ? 4 : 1))) decode_partition_kernel(
     void* __restrict__ out, const char* __restrict__ q, int64_t q_stride_bytes,
     char* __restrict__ k_cache, char* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, int32_t max_blocks,
@@ -509,7 +524,7 @@ __global__ void __launch_bounds__(kThreads) decode_partition_kernel(
   auto score_row = [&](const Vec (&k)[NV1], int tl, bool store) {
     float sc[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) sc[h] = qs[h].dot(k);
+    for (int h = 0; h < G; ++h) sc[h] = qs[h].template dot<BT && G == 8>(k);
     if constexpr (kScatter) {
       Scatter::reduce(sc);
       if (store && (li1 & ((1 << Scatter::TAIL) - 1)) == 0) {
