@@ -32,6 +32,10 @@
 //            and across waves (LDS, fixed order), then either the
 //            normalised output is written (single partition) or the
 //            (max, sum, unnormalised output) partial goes to the workspace.
+// At G >= 8 with blocks of 256 rows or more (and partitions a multiple of
+// 256), a kernel instantiation loads each half-trip of rows through one block
+// lookup and a buffer resource (block trips), and its value pass takes a
+// lane's rows in pairs, one v_dot2 with bf16 weights per element and head.
 // A second kernel merges the partials of a (sequence, query head) with the
 // log-sum-exp rule. Summation order depends only on logical positions, so
 // the result is bitwise independent of where blocks sit in the pool.
