@@ -171,6 +171,11 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  * output) partials to `workspace` and a second kernel merges them with the
  * log-sum-exp rule. The result does not depend on the physical block ids
  * (bitwise), only on the logical history and the partition size.
+ * Precision: fp32 scores, softmax and sums. For bf16 caches (and the fp8
+ * caches of pa_decode_fp8) at group size 8 or 16 with block_size >= 256 and
+ * the partition a multiple of 256 (the library default for such shapes is
+ * one), the softmax weights are rounded to bf16 before they multiply V, as
+ * in pa_prefill_varlen; the products and sums stay fp32.
  *
  *   out           [num_seqs, num_q_heads, head_dim], contiguous.
  *   q             [num_seqs, num_q_heads, head_dim]; row b at q + b * q_row_stride.
