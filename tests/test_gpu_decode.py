@@ -310,18 +310,19 @@ def test_store_decode_matches_separate_calls(dtype, d, g, partition):
 BLOCK_TRIP_CTX = [1, 100, 127, 128, 129, 255, 256, 257, 300, 511, 512, 700, 1023, 1024, 1025, 2000]
 
 
-@pytest.mark.parametrize("g,hkv,d,part", [
-    (8, 2, 128, 256), (8, 2, 128, 512), (8, 2, 128, 1024), (8, 2, 64, 256),
-    (16, 1, 128, 256), (16, 1, 128, 512),
+@pytest.mark.parametrize("g,hkv,d,bs,part", [
+    (8, 2, 128, 256, 256), (8, 2, 128, 256, 512), (8, 2, 128, 256, 1024), (8, 2, 64, 256, 256),
+    (16, 1, 128, 256, 256), (16, 1, 128, 256, 512),
+    (8, 2, 128, 512, 512), (8, 1, 128, 1024, 1024), (16, 1, 64, 512, 256),
 ])
-def test_decode_block_trips(g, hkv, d, part):
-    """Blocks of 256 rows and partitions that are multiples of 256: at G >= 8
-    the launch takes the kernel that loads each half-trip of rows through one
-    block lookup. Split-K launches against the oracle, and the fused call
-    against the two calls bit for bit."""
+def test_decode_block_trips(g, hkv, d, bs, part):
+    """Blocks of 256 rows or more and partitions that are multiples of 256:
+    at G >= 8 the launch takes the kernel that loads each half-trip of rows
+    through one block lookup. Split-K launches against the oracle, and the
+    fused call against the two calls bit for bit."""
     import torch
-    w = wl.custom_decode(BLOCK_TRIP_CTX, block_size=256, num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d,
-                         dtype="bf16", seed=g * 7 + d + part, width=wl.num_blocks_for(2000, 256) + 1)
+    w = wl.custom_decode(BLOCK_TRIP_CTX, block_size=bs, num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d,
+                         dtype="bf16", seed=g * 7 + d + part + bs, width=wl.num_blocks_for(2000, bs) + 1)
     run_small(w, part)
     t = wl.make_host_tensors(w)
     dev = _device_inputs(w, t)

@@ -296,15 +296,18 @@ def test_decode_fp8_block_sizes(bs, ctx):
     run_decode_fp8(wl.with_fp8_cache(w, 0.03, 0.011), 0)
 
 
-@pytest.mark.parametrize("g,hkv,part", [(8, 2, 256), (8, 2, 1024), (16, 1, 512)])
-def test_decode_fp8_block_trips(g, hkv, part):
-    """fp8 caches with blocks of 256 rows and partitions that are multiples
-    of 256 at G >= 8 (the block-trip kernel): contexts ending inside, at and
-    just past half-trips and blocks; two calls and the fused call against the
-    oracle, and against each other bit for bit."""
+@pytest.mark.parametrize("g,hkv,d,bs,part", [
+    (8, 2, 128, 256, 256), (8, 2, 128, 256, 1024), (16, 1, 128, 256, 512),
+    (8, 2, 64, 256, 256), (8, 2, 128, 1024, 1024),
+])
+def test_decode_fp8_block_trips(g, hkv, d, bs, part):
+    """fp8 caches with blocks of 256 rows or more and partitions that are
+    multiples of 256 at G >= 8 (the block-trip kernel): contexts ending
+    inside, at and just past half-trips and blocks; two calls and the fused
+    call against the oracle, and against each other bit for bit."""
     ctx = [1, 100, 127, 128, 129, 255, 256, 257, 300, 511, 512, 700, 1023, 1024, 1025, 2000]
-    w = wl.custom_decode(ctx, block_size=256, num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=128,
-                         dtype="bf16", seed=g + part, width=wl.num_blocks_for(2000, 256) + 1)
+    w = wl.custom_decode(ctx, block_size=bs, num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d,
+                         dtype="bf16", seed=g + part + d + bs, width=wl.num_blocks_for(2000, bs) + 1)
     run_decode_fp8(wl.with_fp8_cache(w, 0.02, 0.015), part)
 
 
