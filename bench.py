@@ -205,6 +205,13 @@ def run_decode(torch, binding, wl, w, steps, warmup, flush, scratch, partition=0
         res[key.replace("_ms", "_GBps")] = res["bytes_logical"] / m / 1e9
         res[key.replace("_ms", "_GBps_unique")] = res["bytes_unique"] / m / 1e9
     res["hbm_frac_unique"] = res["fused_GBps_unique"] / HBM_PEAK_GBS
+    g = w.num_q_heads // w.num_kv_heads
+    tag = "Fp8Tag" if fp8 else ("BF16Tag" if w.elem_bytes == 2 else "float")
+    # block trips (the last template argument) need G >= 8, a 16-bit or fp8 cache and 256+ row blocks;
+    # the partition the library picks decides the rest, so the name says "BT" where they may apply
+    trips = "BT" if g >= 8 and tag != "float" and w.block_size >= 256 else "false"
+    res["kernel"] = (f"pa_store_decode (decode_partition_kernel<{tag}, {w.head_dim}, {g}, true, {trips}> "
+                     f"+ decode_reduce_kernel)")
     del t
     return res
 
@@ -492,7 +499,7 @@ def decode_roofline(res, traffic):
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": traffic,
         "workload": res["workload"],
-        "kernel": "pa_store_decode (decode_partition_kernel<BF16Tag, 128, G, true> + decode_reduce_kernel)",
+        "kernel": res["kernel"],
         "algorithmic_bytes_per_launch": res["fused_bytes"],
         "avg_launch_ms": round(fm, 5),
         "median_launch_ms": round(res["fused_ms"]["median"], 5),

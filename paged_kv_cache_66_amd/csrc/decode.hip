@@ -316,8 +316,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(B
   constexpr int kSecond = kPair ? VB : LPT1 * VB;    // byte offset of the second vector
   constexpr int kFirst = kPair ? 2 * VB : VB;        // bytes between lanes' first vectors
   constexpr int STEP1 = kWaves * TPW1;
-  // rows per lane and loop trip: 256 bytes of loads per lane, at most 16 rows
-  constexpr int kUnroll1 = 256 / (NV1 * VB) < 16 ? 256 / (NV1 * VB) : 16;
+  // rows per lane and loop trip: 256 bytes of loads per lane, at most 16
+  // rows; fp8 at G <= 4 takes 8 rows (128 bytes), which frees the registers
+  // for five or six waves per SIMD instead of four
+  constexpr int kUnroll1 = (kFp8 && G <= 4) ? 8 : (256 / (NV1 * VB) < 16 ? 256 / (NV1 * VB) : 16);
   // value pass: LPT lanes per row, one vector each (fewer accumulators); at
   // G >= 8 (16-bit and fp8 caches) half a vector each (8 bytes, or 4 fp8
   // codes), which halves the G x elements accumulators a lane keeps
@@ -740,9 +742,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(B
     }
   };
 
-  // the same two-half pipelining as the score pass (the first half's loads
-  // were issued before phase 2); every lane still adds its rows in
-  // increasing order
+  // the same two-half pipelining as the score pass; every lane still adds its
+  // rows in increasing order
   if (nloop > 0) {
     auto accum_v = [&](int base, int half) {
       if constexpr (kPairV) {
