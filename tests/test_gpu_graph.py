@@ -43,6 +43,9 @@ HEADS_8B = (32, 8)      # the large-batch decode workload's heads
     (8, 5, SMALL_HEADS, False), (4, 4, SMALL_HEADS, False), (16, 9, SMALL_HEADS, False),
     (1, 1, HEADS_8B, False), (1, 1, HEADS_8B, True),          # the smallest bucket
     (512, 300, HEADS_8B, False), (512, 300, HEADS_8B, True),  # the largest bucket, mostly real rows
+    # the rest of the power-of-two ladder between them
+    (2, 1, HEADS_8B, True), (32, 20, HEADS_8B, False), (64, 64, HEADS_8B, True),
+    (128, 100, HEADS_8B, False), (256, 170, HEADS_8B, True),
 ])
 def test_graph_replay_matches_eager(bucket, real, heads, fused):
     import torch
