@@ -681,15 +681,26 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_direct_kernel(
   const int32_t* table = paged ? block_tables + static_cast<int64_t>(i) * max_blocks : nullptr;
   const int bs_mask = (1 << log2_bs) - 1;
   const int64_t k0_row = paged ? 0 : cu_k[i];
-  auto tile_row0 = [&](int kt0) -> int64_t {  // row index of key kt0 in the K / V tensors
+  // The K (which = 0) and V (which = 1) tile streams each remember the last
+  // block they looked up, so a tile in the same block as its stream's
+  // previous tile needs no table read (three of every four tiles at a block
+  // size of 256: chunked prefill ~1.4 % faster).
+  int cached_bi[2] = {-1, -1};
+  int32_t cached_blk[2] = {0, 0};
+  auto tile_row0 = [&](int kt0, int which) -> int64_t {  // row index of key kt0 in the K / V tensors
     if (paged) {
-      // the block id is uniform: read it through the scalar cache (the
-      // compiler would make it a vector load behind the LDS-bound loads and
-      // wait for those)
-      const int32_t* e = table + (kt0 >> log2_bs);
-      int32_t blk;
-      asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(blk) : "s"(e) : "memory");
-      return (static_cast<int64_t>(blk) << log2_bs) + (kt0 & bs_mask);
+      const int bi = kt0 >> log2_bs;
+      if (bi != cached_bi[which]) {
+        // the block id is uniform: read it through the scalar cache (the
+        // compiler would make it a vector load behind the LDS-bound loads and
+        // wait for those)
+        const int32_t* e = table + bi;
+        int32_t blk;
+        asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(blk) : "s"(e) : "memory");
+        cached_bi[which] = bi;
+        cached_blk[which] = blk;
+      }
+      return (static_cast<int64_t>(cached_blk[which]) << log2_bs) + (kt0 & bs_mask);
     }
     return k0_row + kt0;
   };
@@ -719,8 +730,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_direct_kernel(
   };
   const uint32_t lds_k[2] = {wave_lds(sK[0]), wave_lds(sK[1])};
   const uint32_t lds_v[2] = {wave_lds(sV[0]), wave_lds(sV[1])};
-  auto issue = [&](const char* base, int64_t stride, const uint32_t (&off)[LOADS], uint32_t lds, int kt0) {
-    const uint64_t tile = reinterpret_cast<uint64_t>(base + tile_row0(kt0) * stride + head_off);
+  auto issue = [&](const char* base, int64_t stride, const uint32_t (&off)[LOADS], uint32_t lds, int kt0, int which) {
+    const uint64_t tile = reinterpret_cast<uint64_t>(base + tile_row0(kt0, which) * stride + head_off);
     u32x4_t rs;  // raw buffer resource: base, no stride, 2^31 - 1 bytes
     rs.x = static_cast<uint32_t>(tile);
     rs.y = static_cast<uint32_t>(tile >> 32) & 0xffffu;
@@ -758,7 +769,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_direct_kernel(
     const int64_t stride = is_v ? v_stride_bytes : k_stride_bytes;
     const uint32_t(&off)[LOADS] = is_v ? vload : kload;
     if (!FUSED || kt0 + kKeys <= start) {
-      issue(cache, stride, off, lds, kt0);
+      issue(cache, stride, off, lds, kt0, is_v ? 1 : 0);
       return;
     }
     const char* nb = is_v ? new_v : new_k;
@@ -783,7 +794,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_direct_kernel(
       }
       return;
     }
-    const int64_t crow0 = tile_row0(kt0);
+    const int64_t crow0 = tile_row0(kt0, is_v ? 1 : 0);
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       const int r = min(lrow[j], rmax);
