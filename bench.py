@@ -510,7 +510,7 @@ def decode_roofline(res, traffic):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     import torch
