@@ -59,7 +59,8 @@ def test_stored_traffic_only_for_matching_sources(tmp_path, monkeypatch):
 
 
 def test_committed_traffic_files_are_well_formed():
-    for name, kind in (("8b-decode-bs16", "decode"), ("long-context-decode", "decode"),
+    for name, kind in (("8b-decode-bs16", "decode"), ("8b-decode-bs256", "decode"),
+                       ("qwen3-0.6b-decode", "decode"), ("long-context-decode", "decode"),
                        ("chunked-prefill", "prefill")):
         with open(bench.traffic_file(name)) as f:
             rec = json.load(f)
